@@ -1,0 +1,414 @@
+"""Decode throughput of the ReplaySSM kernels on one MI355X.
+
+Headline: Mamba2 ReplaySSM decode (replayssm_decode) at batch 512, 80 heads,
+headdim 64, dstate 128, ngroups 1, ring L = 16, bf16 inputs and bf16 state
+pool (fp32 arithmetic), start positions uniform in [0, L) so flush rows
+interleave every step.  One step = one replayssm_decode launch over the whole
+batch for one layer; ``--layers`` independent layers (state pool + rings +
+cursors each) are used round-robin so a checkpoint is re-read only after the
+other layers' ~2.7 GB have streamed (far beyond the 256 MB last-level cache).
+value = batch * steps / seconds (state-updates/s: one row advanced one step
+through one layer).
+
+Also measured in the same run (separate timed regions): the standard
+read+write update (ssu_standard_decode) on the same workload, and the GDN
+replay/standard decode at batch 256 (16 key / 32 value heads, K = V = 128,
+L = 16, bf16 q/k/v, fp32 state); and the float64 CPU oracle on a bounded
+sample (``cpu_baseline``).
+
+Roofline: algorithmic bytes per launch (checkpoint reads, ring reads of the
+live entries, ring appends, flush write-backs, step inputs, outputs and
+metadata, evaluated exactly from every row's cursor at that step) divided by
+the average launch time measured with HIP events on the launch stream.
+``traffic`` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters when given
+with --traffic-json (see profiles/).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 4]
+       python bench.py --copy-probe      (copy kernel for counter calibration)
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "decode state-updates/s + achieved HBM GB/s (% peak), Mamba2 B=512 L=16"
+
+
+def _sizes(dt):
+    return 2 if dt == torch.bfloat16 else 4
+
+
+class Mamba2Layers:
+    """`layers` independent Mamba2 layers of one workload, resident on the GPU."""
+
+    def __init__(self, wl, layers, dev, y_dtype, seed=7):
+        from workloads import TORCH_DTYPES, Mamba2Inputs, device_normal_
+        self.wl, self.dev, self.nl = wl, dev, layers
+        gen = Mamba2Inputs(wl)
+        self.gen = gen
+        H, P, N, G, L, ns = wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.ring_len, wl.num_slots
+        io = TORCH_DTYPES[wl.io_dtype]
+        sdt = TORCH_DTYPES[wl.state_dtype]
+        self.io, self.sdt, self.y_dtype = io, sdt, y_dtype
+        self.prm = {k: v.to(dev) for k, v in gen.params().items()}
+        self.slots = gen.slot_idx().to(dev)
+        self.w0 = gen.start_positions().numpy()
+        self.state, self.xr, self.dr, self.br = [], [], [], []
+        self.std_state = []
+        for l in range(layers):
+            st = torch.empty((ns, H, P, N), dtype=sdt, device=dev)
+            device_normal_(st, 0.1, seed + l)
+            self.state.append(st)
+            self.xr.append(torch.zeros((ns, H, L, P), dtype=io, device=dev))
+            self.dr.append(torch.zeros((ns, H, L), dtype=torch.float32, device=dev))
+            self.br.append(torch.zeros((ns, G, L, N), dtype=io, device=dev))
+        nb = wl.batch
+        self.wp = [torch.zeros(nb, dtype=torch.int32, device=dev) for _ in range(layers)]
+        self.fl = [torch.full((nb,), 1 if L == 1 else 0, dtype=torch.uint8, device=dev)
+                   for _ in range(layers)]
+        self.nwp = [torch.empty_like(t) for t in self.wp]
+        self.nfl = [torch.empty_like(t) for t in self.fl]
+        self.steps_done = [0] * layers
+        self.inputs = [{k: v.to(dev) for k, v in gen.step(t).items()} for t in range(8)]
+        self.y = torch.empty((nb, H, P), dtype=y_dtype, device=dev)
+        # per-row byte accounting
+        sst, sio, sy = _sizes(sdt), _sizes(io), _sizes(y_dtype)
+        self.tile = H * P * N * sst
+        self.entry = H * P * sio + G * N * sio + 4 * H
+        self.inp = 2 * H * P * sio + H * sio + 2 * G * N * sio + H * P * sy
+        self.params = 3 * 4 * H
+
+    def warm_rings(self):
+        """Run the L warm-up steps that leave row r with w0[r] ring entries."""
+        L = self.wl.ring_len
+        for l in range(self.nl):
+            for k in range(L):
+                force = self.gen.warm_force_flush(k).to(self.dev)
+                self.fl[l] |= force
+                self.replay(l, self.inputs[k % 8])
+            self.steps_done[l] = 0
+        torch.cuda.synchronize()
+        for l in range(self.nl):
+            assert np.array_equal(self.wp[l].cpu().numpy(), self.w0), "warm-up cursors"
+
+    def replay(self, l, inp):
+        import linear_recurrence_amd as R
+        R.replayssm_decode(self.state[l], self.xr[l], self.dr[l], self.br[l], self.slots,
+                           self.wp[l], self.fl[l], inp["x"], inp["dt"], self.prm["A"],
+                           inp["B"], inp["C"], D=self.prm["D"], z=inp["z"],
+                           dt_bias=self.prm["dt_bias"], y=self.y,
+                           next_write_pos=self.nwp[l], next_is_flush=self.nfl[l])
+        self.wp[l], self.nwp[l] = self.nwp[l], self.wp[l]
+        self.fl[l], self.nfl[l] = self.nfl[l], self.fl[l]
+
+    def standard(self, l, inp):
+        import linear_recurrence_amd as R
+        R.ssu_standard_decode(self.state[l], self.slots, inp["x"], inp["dt"], self.prm["A"],
+                              inp["B"], inp["C"], D=self.prm["D"], z=inp["z"],
+                              dt_bias=self.prm["dt_bias"], y=self.y)
+
+    def replay_bytes(self, step_in_layer):
+        """Algorithmic bytes of one replay launch, from every row's cursor."""
+        L = self.wl.ring_len
+        w = (self.w0 + step_in_layer) % L
+        flush = w == L - 1
+        per_row = (self.tile + w * self.entry + np.where(flush, self.tile, self.entry)
+                   + self.inp + 14)
+        return float(per_row.sum() + self.params)
+
+    def standard_bytes(self):
+        return float(self.wl.batch * (2 * self.tile + self.inp + 4) + self.params)
+
+
+def time_region(fn, steps, warmup):
+    """W untimed steps, then exactly K timed steps between synchronisations."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(warmup + i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3  # seconds
+
+
+def bench_mamba2(wl, layers, steps, warmup, y_dtype, dev):
+    M = Mamba2Layers(wl, layers, dev, y_dtype)
+    M.warm_rings()
+    # replay: step i uses layer i % layers; bytes are accounted per launch
+    # from the cursors that layer has at that step
+    step_of = [0] * layers
+
+    def rep(i):
+        l = i % layers
+        M.replay(l, M.inputs[i % 8])
+        step_of[l] += 1
+
+    for i in range(warmup):
+        rep(i)
+    torch.cuda.synchronize()
+    local = list(step_of)
+    total_bytes = 0.0
+    for i in range(steps):
+        l = (warmup + i) % layers
+        total_bytes += M.replay_bytes(local[l])
+        local[l] += 1
+    t_rep = time_region(lambda i: rep(warmup + i), steps, 0)
+    for l in range(layers):
+        got = M.wp[l].cpu().numpy()
+        assert np.array_equal(got, (M.w0 + step_of[l]) % wl.ring_len), "cursor drift"
+    rep_bytes = total_bytes / steps
+
+    def std(i):
+        M.standard(i % layers, M.inputs[i % 8])
+
+    t_std = time_region(std, steps, warmup)
+    std_bytes = M.standard_bytes()
+    nb = wl.batch
+    res = {
+        "replay_s": t_rep, "standard_s": t_std,
+        "replay_bytes_per_launch": rep_bytes, "standard_bytes_per_launch": std_bytes,
+        "replay_updates_per_s": nb * steps / t_rep,
+        "standard_updates_per_s": nb * steps / t_std,
+        "replay_GBps": rep_bytes * steps / t_rep / 1e9,
+        "standard_GBps": std_bytes * steps / t_std / 1e9,
+    }
+    del M
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_gdn(wl, layers, steps, warmup, dev):
+    import linear_recurrence_amd as R
+    from workloads import TORCH_DTYPES, GdnInputs, device_normal_
+    gen = GdnInputs(wl)
+    HK, HV, K, V, L, ns, nb = wl.k_heads, wl.v_heads, wl.dk, wl.dv, wl.ring_len, wl.num_slots, wl.batch
+    io = TORCH_DTYPES[wl.io_dtype]
+    states = []
+    for l in range(layers):
+        st = torch.empty((ns, HV, V, K), dtype=torch.float32, device=dev)
+        device_normal_(st, 0.1, 100 + l)
+        states.append(st)
+    dr = [torch.zeros((ns, HV, L, V), device=dev) for _ in range(layers)]
+    kr = [torch.zeros((ns, HK, L, K), dtype=io, device=dev) for _ in range(layers)]
+    gr = [torch.zeros((ns, HV, L), device=dev) for _ in range(layers)]
+    wp = [torch.zeros(nb, dtype=torch.int32, device=dev) for _ in range(layers)]
+    fl = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(layers)]
+    nwp = [torch.empty_like(t) for t in wp]
+    nfl = [torch.empty_like(t) for t in fl]
+    slots = gen.slot_idx().to(dev)
+    inputs = [{k: v.to(dev) for k, v in gen.step(t).items()} for t in range(8)]
+    o = torch.empty((nb, HV, V), dtype=io, device=dev)
+
+    def rep(i):
+        l = i % layers
+        inp = inputs[i % 8]
+        R.replayssm_gdn_decode(states[l], dr[l], kr[l], gr[l], slots, wp[l], fl[l], inp["q"],
+                               inp["k"], inp["v"], inp["g"], inp["beta"], o=o,
+                               next_write_pos=nwp[l], next_is_flush=nfl[l])
+        wp[l], nwp[l] = nwp[l], wp[l]
+        fl[l], nfl[l] = nfl[l], fl[l]
+
+    def std(i):
+        l = i % layers
+        inp = inputs[i % 8]
+        R.gdn_standard_decode(states[l], slots, inp["q"], inp["k"], inp["v"], inp["g"],
+                              inp["beta"], o=o)
+
+    # whole ring periods per layer keep the flush share exact (lock-step rows)
+    steps_r = max(layers * L, (steps // (layers * L)) * layers * L)
+    warm_r = layers * L
+    t_rep = time_region(rep, steps_r, warm_r)
+    t_std = time_region(std, steps, warmup)
+    sio = _sizes(io)
+    tile = HV * V * K * 4
+    entry = HV * V * 4 + HK * K * sio + HV * 4
+    inp_b = 2 * HK * K * sio + HV * V * sio + 2 * HV * 4 + HV * V * sio
+    # lock-step rows: over a ring period the positions are 0..L-1 once each
+    ring_reads = sum(range(L)) / L * entry
+    per_row_rep = tile + ring_reads + (L - 1) / L * entry + tile / L + inp_b + 14
+    per_row_std = 2 * tile + inp_b + 4
+    res = {
+        "workload": wl.name,
+        "replay_updates_per_s": nb * steps_r / t_rep,
+        "standard_updates_per_s": nb * steps / t_std,
+        "replay_GBps": per_row_rep * nb * steps_r / t_rep / 1e9,
+        "standard_GBps": per_row_std * nb * steps / t_std / 1e9,
+        "replay_us_per_step": t_rep / steps_r * 1e6,
+        "standard_us_per_step": t_std / steps * 1e6,
+    }
+    res["speedup"] = res["replay_updates_per_s"] / res["standard_updates_per_s"]
+    del states, dr, kr, gr
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(wl, rows, steps):
+    """The float64 oracle's replay step on a bounded sample of the workload:
+    `rows` rows of the batch for `steps` steps from its first (desync) warm-up
+    step, single-threaded; inputs drawn before the clock starts."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import mamba2 as OM
+    from workloads import Mamba2Inputs
+    gen = Mamba2Inputs(wl)
+    H, P, N, G, L = wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.ring_len
+    slots = gen.slot_idx().numpy()[:rows]
+    pool = np.stack([gen.slot_state(int(s)).double().numpy() for s in slots])
+    prm = {n: v.double().numpy() for n, v in gen.params().items()}
+    xr = np.full((rows, H, L, P), np.nan)
+    dr = np.full((rows, H, L), np.nan)
+    br = np.full((rows, G, L, N), np.nan)
+    wp = np.zeros(rows, np.int32)
+    fl = np.zeros(rows, np.uint8)
+    seq = []
+    for t in range(steps):
+        src = gen.warm_step(t) if t < L else gen.step(t - L)
+        force = gen.warm_force_flush(t).numpy()[:rows] if t < L else np.zeros(rows, np.uint8)
+        seq.append(({n: v[:rows].double().numpy() for n, v in src.items()}, force))
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for inp, force in seq:
+            fl = fl | force
+            _, wp, fl, _ = OM.replay_step(pool, xr, dr, br, np.arange(rows), wp, fl, inp["x"],
+                                          inp["dt"], prm["A"], inp["B"], inp["C"], D=prm["D"],
+                                          z=inp["z"], dt_bias=prm["dt_bias"],
+                                          state_dtype=wl.state_dtype)
+        dt = time.perf_counter() - t0
+    return {"value": rows * steps / dt, "unit": "state-updates/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"float64 NumPy replay oracle, {rows} of {wl.batch} rows x {steps} "
+                      f"steps ({L} desync warm-up steps first), one thread, {dt:.1f} s"}
+
+
+def copy_probe(dev, gib=1.0, reps=5):
+    """A plain device copy of known size, for scaling HBM counters."""
+    n = int(gib * (1 << 30)) // 4
+    a = torch.empty(n, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    t = time_region(lambda i: b.copy_(a), reps, 1)
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "dispatches": reps + 1 + reps,
+                      "copy_GBps": 2 * n * 4 * reps / t / 1e9}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--y-dtype", choices=("bf16", "f32"), default="bf16")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-gdn", action="store_true", help="skip the GDN measurement")
+    ap.add_argument("--cpu-rows", type=int, default=48)
+    ap.add_argument("--cpu-steps", type=int, default=32)
+    ap.add_argument("--traffic-json", default=None,
+                    help="per-launch HBM bytes measured with rocprofv3 counters")
+    ap.add_argument("--copy-probe", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the decode path has no cross-GPU exchange "
+              "(rows and heads shard with zero communication), so only --gpus 1 is "
+              "supported.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import linear_recurrence_amd as R
+    R.load()
+    dev = torch.device("cuda:0")
+    if args.copy_probe:
+        copy_probe(dev)
+        return
+
+    from workloads import GDN, LARGE_BATCH
+    wl = LARGE_BATCH
+    y_dtype = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
+    print(f"[bench] {wl.name}: layers={args.layers} steps={args.steps} warmup={args.warmup}",
+          file=sys.stderr, flush=True)
+    m = bench_mamba2(wl, args.layers, args.steps, args.warmup, y_dtype, dev)
+    print(f"[bench] mamba2 done: {m['replay_GBps']:.0f} GB/s replay, "
+          f"{m['standard_GBps']:.0f} GB/s standard", file=sys.stderr, flush=True)
+    gdn = None
+    if not args.no_gdn:
+        gdn = bench_gdn(GDN, args.layers, args.steps, args.warmup, dev)
+        print(f"[bench] gdn done: {gdn['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
+              flush=True)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, args.cpu_rows, args.cpu_steps)
+        print(f"[bench] cpu oracle done: {cpu['sample']}", file=sys.stderr, flush=True)
+
+    ms_per_step = m["replay_s"] / args.steps * 1e3
+    achieved = m["replay_bytes_per_launch"] / (m["replay_s"] / args.steps) / 1e9
+    traffic = None
+    if args.traffic_json:
+        with open(args.traffic_json) as fh:
+            traffic = json.load(fh).get("replayssm_decode_bytes_per_launch")
+    line = {
+        "metric": METRIC,
+        "value": m["replay_updates_per_s"],
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name, "batch": wl.batch, "nheads": wl.nheads,
+            "headdim": wl.headdim, "dstate": wl.dstate, "ngroups": wl.ngroups,
+            "ring_len": wl.ring_len, "num_slots": wl.num_slots,
+            "io_dtype": wl.io_dtype, "state_dtype": wl.state_dtype,
+            "y_dtype": args.y_dtype, "layers_rotated": args.layers,
+            "start_positions": "uniform in [0, L)",
+        },
+        "hbm_GBps": achieved,
+        "hbm_frac_of_peak": achieved / PEAK_HBM_GBPS,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+            "kernel": "replayssm_decode (mamba2_decode_kernel, replay)",
+            "algorithmic_bytes_per_launch": m["replay_bytes_per_launch"],
+        },
+        "cpu_baseline": cpu,
+        "standard": {
+            "kernel": "ssu_standard_decode",
+            "state_updates_per_s": m["standard_updates_per_s"],
+            "ms_per_step": m["standard_s"] / args.steps * 1e3,
+            "achieved_GBps": m["standard_GBps"],
+            "frac": m["standard_GBps"] / PEAK_HBM_GBPS,
+            "bytes_per_launch": m["standard_bytes_per_launch"],
+        },
+        "speedup_vs_standard": m["replay_updates_per_s"] / m["standard_updates_per_s"],
+        "gdn": gdn,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,234 @@
+/*
+ * replayssm.h - C ABI of the MI355X (gfx950) ReplaySSM decode library.
+ *
+ * One decode step of a Mamba2 selective state update for a batch of rows,
+ * either the standard read+write update or the ReplaySSM output-only form
+ * (a checkpoint S0 plus a per-slot ring of the last inputs, folded into the
+ * state only on flush rows), plus the gated-delta-rule (GDN) counterparts.
+ *
+ * Sources (page title, then section):
+ *  - vLLM #48018 "[Kernel] ReplaySSM: cache SSM inputs for faster Mamba2
+ *    standard decode": Motivation (state traffic; ring + periodic checkpoint;
+ *    write-back once every L steps), Implementation items 1-3 (per-row
+ *    is_flush branch; x/dt/B ring caches; per-row write_pos and is_flush
+ *    from the metadata builder), key source snippet of mamba_mixer2.py (the
+ *    argument lists of the replay op and of the baseline update).
+ *  - sglang #28451 (GDN/KDA ReplaySSM decode): Motivation and Implementation
+ *    items 1-3 (GDN ring decode, static cursor buffers, copy rules).
+ *  - sglang #28695 "[GDN] Support ReplaySSM Ring Spec-Verify": memory-pool
+ *    snippet (the GDN ring holds d [L,V], k [L,K], g [L] per slot).
+ *  - vLLM #52506 "[Mamba] Add FlashInfer ReplaySSM backend": Implementation
+ *    item 1 (ring cursors are reset when a slot is reused).
+ *
+ * Conventions shared by every entry point
+ *  - Every pointer is a DEVICE pointer to memory the caller owns, allocated
+ *    on the device that is current when the call is made.  The library never
+ *    allocates, frees or synchronises, keeps no global mutable state, and is
+ *    re-entrant: it validates the arguments, enqueues kernels on `stream`
+ *    (0 = the null stream) and returns.
+ *  - All tensors are dense, row-major (last index fastest), with no padding.
+ *    Pointers accessed with 16-byte vector loads (marked [16B]) must be
+ *    16-byte aligned.
+ *  - Element types follow the *_dtype fields (RSSM_F32 = float, RSSM_BF16 =
+ *    bfloat16 bit pattern).  A, D, dt_bias, dt_ring, the GDN d/g rings, g and
+ *    beta are always float32.  bf16 stores round to nearest even from the
+ *    fp32 value; all arithmetic is fp32.
+ *  - Return value: RSSM_OK (0) or a negative RSSM_E* code (nothing is
+ *    enqueued on an error other than RSSM_ELAUNCH).  No exception crosses
+ *    the ABI.
+ *  - Device-side metadata errors do not fail the call: the kernel ORs
+ *    RSSM_ST_* bits into *status (if status != NULL) and handles the row
+ *    safely; outputs of such rows are unspecified (y is NaN for bad slots).
+ *  - Contract: slot indices within one call are distinct; the next_* cursor
+ *    buffers do not alias write_pos / is_flush.  Calls that share a state
+ *    pool or rings must be ordered by the caller (same stream or events).
+ */
+#ifndef REPLAYSSM_H
+#define REPLAYSSM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum { RSSM_F32 = 0, RSSM_BF16 = 1 };
+
+/* return codes */
+enum {
+  RSSM_OK = 0,
+  RSSM_EINVAL = -1,      /* NULL required pointer, bad size, misalignment, aliasing */
+  RSSM_EDTYPE = -2,      /* unsupported dtype combination */
+  RSSM_ELAUNCH = -3,     /* the kernel launch reported an error */
+  RSSM_ESHAPE = -4       /* headdim / dstate / ring length not supported */
+};
+
+/* device status bits (ORed into *status) */
+enum {
+  RSSM_ST_BAD_WRITE_POS = 1, /* write_pos outside [0, L): clamped, row flushed */
+  RSSM_ST_RING_OVERFLOW = 2, /* write_pos == L-1 without is_flush: row flushed */
+  RSSM_ST_BAD_SLOT = 4,      /* slot index outside [0, num_slots): row skipped */
+  RSSM_ST_BAD_ROW = 8        /* ring reset: row index outside [0, batch) */
+};
+
+/*
+ * Mamba2 dimensions.  Supported: headdim in {32, 64, 128}; dstate in {16,
+ * 32, 64, 128, 256}; 1 <= ring_len <= 64 with the ring rows a workgroup
+ * stages, about 4*ring_len*(P+N) bytes, within 64 KB (RSSM_ESHAPE otherwise);
+ * ngroups divides nheads; state,
+ * io and out dtypes each RSSM_F32 or RSSM_BF16.
+ */
+typedef struct rssm_dims {
+  int32_t batch;       /* decode rows (0: return RSSM_OK, read nothing)     */
+  int32_t nheads;      /* H                                                 */
+  int32_t headdim;     /* P                                                 */
+  int32_t dstate;      /* N                                                 */
+  int32_t ngroups;     /* G: head h reads B/C group h / (H / G)             */
+  int32_t ring_len;    /* L (ignored by ssu_standard_decode)                */
+  int32_t num_slots;   /* first dimension of the state pool and the rings   */
+  int32_t state_dtype; /* state pool                                        */
+  int32_t io_dtype;    /* x, z, dt, B, C and the x / B rings                */
+  int32_t out_dtype;   /* y                                                 */
+  int32_t dt_softplus; /* nonzero: dt = softplus(dt + dt_bias)              */
+} rssm_dims;
+
+/*
+ * ssu_standard_decode - the standard selective state update (the baseline
+ * the replay is measured against; vLLM #48018, Motivation and the baseline
+ * call in the mamba_mixer2.py snippet).  For each row b, head h, with
+ * s = slot_idx[b], g = h / (H/G):
+ *     dt = softplus(dt[b,h] + dt_bias[h])      (no softplus if !dt_softplus)
+ *     S  = exp(dt*A[h]) * state[s,h] + dt * outer(x[b,h,:], B[b,g,:])
+ *     y[b,h,:] = S @ C[b,g,:] + D[h] * x[b,h,:];   y *= z * sigmoid(z)
+ *     state[s,h] = S
+ *
+ *   state   [num_slots, H, P, N]  state_dtype   [16B] read and written
+ *   slot_idx [batch] int32        pool slot of each row
+ *   x, z    [batch, H, P]         io_dtype      [16B] z may be NULL (no gate)
+ *   dt      [batch, H]            io_dtype      raw dt
+ *   A       [H] float32; D [H] float32 or NULL; dt_bias [H] float32 or NULL
+ *   B, C    [batch, G, N]         io_dtype      [16B]
+ *   y       [batch, H, P]         out_dtype     written
+ *   status  int32 or NULL         RSSM_ST_BAD_SLOT rows are skipped
+ */
+int ssu_standard_decode(const rssm_dims* dims, void* state,
+                        const int32_t* slot_idx, const void* x, const void* dt,
+                        const float* A, const void* B, const void* C,
+                        const float* D, const void* z, const float* dt_bias,
+                        void* y, int32_t* status, hipStream_t stream);
+
+/*
+ * replayssm_decode - one ReplaySSM output-only decode step (vLLM #48018,
+ * Motivation and Implementation item 1).  Row b with s = slot_idx[b],
+ * w = write_pos[b], f = is_flush[b] uses ring entries 0..w-1 of slot s and
+ * the current step as entry w.  With T = sum_{j<=w} dt_j and
+ * r_i = sum_{i<j<=w} dt_j (dt_j after softplus):
+ *     cumdecay = exp(A[h]*T),  wt_i = dt_i * exp(A[h]*r_i)
+ *     y = cumdecay*(S0 @ C) + sum_{i<=w} wt_i*(B_i . C)*x_i + D*x_w; gate
+ *   f == 0: (x_w, dt_w, B_w) is written at ring position w; the state is not
+ *           touched; next position w+1.
+ *   f != 0: S_new = cumdecay*S0 + sum_{i<=w} wt_i*outer(x_i, B_i) is written
+ *           to state[s,h]; y = S_new @ C + D*x_w (gated); next position 0.
+ *   next_write_pos[b] = next position; next_is_flush[b] = (next == L-1).
+ * A flush may be requested early (w < L-1).  write_pos == L-1 without
+ * is_flush sets RSSM_ST_RING_OVERFLOW and the row is flushed.
+ *
+ *   state    [num_slots, H, P, N]  state_dtype  [16B] checkpoints S0
+ *   x_ring   [num_slots, H, L, P]  io_dtype     [16B] stored x (bit copies)
+ *   dt_ring  [num_slots, H, L]     float32      stored dt after softplus
+ *   B_ring   [num_slots, G, L, N]  io_dtype     [16B] stored B (bit copies)
+ *   slot_idx [batch] int32; write_pos [batch] int32; is_flush [batch] uint8
+ *   next_write_pos [batch] int32 or NULL; next_is_flush [batch] uint8 or NULL
+ *   x, dt, A, B, C, D, z, dt_bias, y: as for ssu_standard_decode
+ *   status   int32 or NULL
+ * Ring entries at positions >= write_pos are never read.
+ */
+int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring,
+                     float* dt_ring, void* B_ring, const int32_t* slot_idx,
+                     const int32_t* write_pos, const uint8_t* is_flush,
+                     int32_t* next_write_pos, uint8_t* next_is_flush,
+                     const void* x, const void* dt, const float* A,
+                     const void* B, const void* C, const float* D,
+                     const void* z, const float* dt_bias, void* y,
+                     int32_t* status, hipStream_t stream);
+
+/*
+ * replayssm_ring_reset - rows whose slot just received a fresh checkpoint
+ * restart with an empty ring (vLLM #52506, Implementation item 1; sglang
+ * #28451, Implementation item 3): for r in rows[0..n_rows):
+ *     write_pos[r] = 0;  is_flush[r] = (ring_len == 1)
+ * Uses dims->batch (row bound) and dims->ring_len only.  The caller writes
+ * the fresh state itself.  rows is a device array; rows outside [0, batch)
+ * are skipped and set RSSM_ST_BAD_ROW in *status (if not NULL).
+ */
+int replayssm_ring_reset(const rssm_dims* dims, int32_t* write_pos,
+                         uint8_t* is_flush, const int32_t* rows,
+                         int32_t n_rows, int32_t* status, hipStream_t stream);
+
+/*
+ * GDN dimensions.  Supported: dk == dv == 128 (also 64); v_heads a multiple
+ * of k_heads (value head hv reads key head hv / (v_heads / k_heads));
+ * 1 <= ring_len <= 64 with 4*ring_len*(K+V) bytes within 64 KB; state_dtype RSSM_F32; io_dtype (q, k, v, k ring) and
+ * out_dtype RSSM_F32 or RSSM_BF16.  scale <= 0 selects 1/sqrt(dk).
+ */
+typedef struct rssm_gdn_dims {
+  int32_t batch;
+  int32_t k_heads;
+  int32_t v_heads;
+  int32_t dk;          /* K */
+  int32_t dv;          /* V */
+  int32_t ring_len;
+  int32_t num_slots;
+  int32_t state_dtype;
+  int32_t io_dtype;
+  int32_t out_dtype;
+  float scale;
+} rssm_gdn_dims;
+
+/*
+ * gdn_standard_decode - the recurrent gated delta rule (sglang #28451,
+ * Motivation: each step reads and writes the full [HV, V, K] state):
+ *     S = g*S;  S += beta * outer(v - S@k, k);  o = scale * S@q
+ *   state [num_slots, HV, V, K] float32 [16B]; slot_idx [batch] int32
+ *   q, k [batch, HK, K] io_dtype [16B]; v [batch, HV, V] io_dtype [16B]
+ *   g, beta [batch, HV] float32 (already activated); o [batch, HV, V] out_dtype
+ */
+int gdn_standard_decode(const rssm_gdn_dims* dims, void* state,
+                        const int32_t* slot_idx, const void* q, const void* k,
+                        const void* v, const float* g, const float* beta,
+                        void* o, int32_t* status, hipStream_t stream);
+
+/*
+ * replayssm_gdn_decode - GDN ReplaySSM decode (sglang #28451, Implementation
+ * item 1; ring contents per sglang #28695, memory-pool snippet).  With
+ * Gamma = prod_{j<=w} g_j and gamma_i = prod_{i<j<=w} g_j:
+ *     pred = Gamma*(S0@k_w) + sum_{i<w} gamma_i*d_i*(k_i . k_w)
+ *     d_w  = beta_w*(v_w - pred)
+ *     o    = scale*[Gamma*(S0@q) + sum_{i<=w} gamma_i*d_i*(k_i . q)]
+ *   f == 0: (d_w, k_w, g_w) written at ring position w;
+ *   f != 0: state = Gamma*S0 + sum_{i<=w} gamma_i*outer(d_i, k_i).
+ *   d_ring [num_slots, HV, L, V] float32 [16B]; k_ring [num_slots, HK, L, K]
+ *   io_dtype [16B] (bit copies of k); g_ring [num_slots, HV, L] float32.
+ *   Cursor and status rules as for replayssm_decode.
+ */
+int replayssm_gdn_decode(const rssm_gdn_dims* dims, void* state, float* d_ring,
+                         void* k_ring, float* g_ring, const int32_t* slot_idx,
+                         const int32_t* write_pos, const uint8_t* is_flush,
+                         int32_t* next_write_pos, uint8_t* next_is_flush,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, void* o,
+                         int32_t* status, hipStream_t stream);
+
+/* Human-readable text of a return code (static storage). */
+const char* replayssm_strerror(int code);
+
+/* Library ABI version (major * 100 + minor). */
+int replayssm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REPLAYSSM_H */

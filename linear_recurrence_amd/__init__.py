@@ -1,0 +1,301 @@
+"""Python binding of libreplayssm (the MI355X ReplaySSM decode library).
+
+Argument marshalling only: every function infers the dimensions from the
+tensors, checks devices, dtypes, shapes and contiguity, and passes raw
+device pointers plus the current HIP stream to the C ABI declared in
+``include/replayssm.h``.  All arithmetic runs in the library's HIP kernels.
+PyTorch supplies device memory and streams.
+
+The library must have been built (``python -m linear_recurrence_amd._build``
+or ``__graft_entry__.build()``); importing the binding without it, or calling
+it on tensors that are not on a GPU, raises instead of computing anything
+elsewhere.
+"""
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime the library then binds to
+
+__all__ = [
+    "ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
+    "gdn_standard_decode", "replayssm_gdn_decode", "library_path", "load",
+    "RssmError", "ST_BAD_WRITE_POS", "ST_RING_OVERFLOW", "ST_BAD_SLOT",
+    "ST_BAD_ROW", "EXPORTS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libreplayssm.so")
+
+F32, BF16 = 0, 1
+ST_BAD_WRITE_POS, ST_RING_OVERFLOW, ST_BAD_SLOT, ST_BAD_ROW = 1, 2, 4, 8
+EXPORTS = ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
+           "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_strerror",
+           "replayssm_abi_version")
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+class RssmError(RuntimeError):
+    def __init__(self, fn, code, msg):
+        super().__init__(f"{fn} failed with code {code}: {msg}")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "nheads", "headdim", "dstate", "ngroups", "ring_len",
+        "num_slots", "state_dtype", "io_dtype", "out_dtype", "dt_softplus")]
+
+
+class GdnDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "batch", "k_heads", "v_heads", "dk", "dv", "ring_len", "num_slots",
+        "state_dtype", "io_dtype", "out_dtype")] + [("scale", ctypes.c_float)]
+
+
+_lib = None
+
+
+def library_path():
+    return LIB_PATH
+
+
+def load():
+    """Load libreplayssm.so (once); raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m linear_recurrence_amd._build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int32
+    lib.ssu_standard_decode.argtypes = [ctypes.POINTER(Dims)] + [P] * 13
+    lib.replayssm_decode.argtypes = [ctypes.POINTER(Dims)] + [P] * 20
+    lib.replayssm_ring_reset.argtypes = [ctypes.POINTER(Dims), P, P, P, I, P, P]
+    lib.gdn_standard_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 10
+    lib.replayssm_gdn_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 17
+    for fn in ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
+               "gdn_standard_decode", "replayssm_gdn_decode"):
+        getattr(lib, fn).restype = ctypes.c_int
+    lib.replayssm_strerror.argtypes = [ctypes.c_int]
+    lib.replayssm_strerror.restype = ctypes.c_char_p
+    lib.replayssm_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(fn, rc):
+    if rc != 0:
+        raise RssmError(fn, rc, load().replayssm_strerror(rc).decode())
+
+
+def _need(t, name, dtype=None, shape=None, dev=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _opt(t, *a, **k):
+    return None if t is None else _need(t, *a, **k)
+
+
+def _mamba2_dims(state, x, B, ring_len, y_dtype, dt_softplus):
+    ns, H, P, N = state.shape
+    nb = x.shape[0]
+    G = B.shape[1]
+    if state.dtype not in _DT or x.dtype not in _DT or y_dtype not in _DT:
+        raise ValueError("dtypes must be float32 or bfloat16")
+    return Dims(nb, H, P, N, G, ring_len, ns, _DT[state.dtype], _DT[x.dtype],
+                _DT[y_dtype], 1 if dt_softplus else 0)
+
+
+def ssu_standard_decode(state, slot_idx, x, dt, A, B, C, D=None, z=None,
+                        dt_bias=None, y=None, dt_softplus=True, status=None,
+                        out_dtype=None, stream=None):
+    """Standard selective state update (reads and writes ``state``); returns y."""
+    dev = _need(state, "state").device
+    ns, H, P, N = state.shape
+    _need(x, "x", (torch.float32, torch.bfloat16), dev=dev)
+    nb = x.shape[0]
+    io = x.dtype
+    _need(x, "x", io, (nb, H, P))
+    _need(B, "B", io, dev=dev)
+    G = B.shape[1]
+    _need(B, "B", io, (nb, G, N))
+    _need(C, "C", io, (nb, G, N))
+    _need(dt, "dt", io, (nb, H))
+    _need(A, "A", torch.float32, (H,))
+    _need(slot_idx, "slot_idx", torch.int32, (nb,))
+    _opt(D, "D", torch.float32, (H,))
+    _opt(z, "z", io, (nb, H, P))
+    _opt(dt_bias, "dt_bias", torch.float32, (H,))
+    _opt(status, "status", torch.int32, (1,))
+    if y is None:
+        y = torch.empty((nb, H, P), dtype=out_dtype or io, device=dev)
+    _need(y, "y", (torch.float32, torch.bfloat16), (nb, H, P), dev=dev)
+    d = _mamba2_dims(state, x, B, 1, y.dtype, dt_softplus)
+    rc = load().ssu_standard_decode(
+        ctypes.byref(d), _ptr(state), _ptr(slot_idx), _ptr(x), _ptr(dt), _ptr(A),
+        _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(y), _ptr(status),
+        _stream(stream))
+    _check("ssu_standard_decode", rc)
+    return y
+
+
+def replayssm_decode(state, x_ring, dt_ring, B_ring, slot_idx, write_pos,
+                     is_flush, x, dt, A, B, C, D=None, z=None, dt_bias=None,
+                     y=None, next_write_pos=None, next_is_flush=None,
+                     dt_softplus=True, status=None, out_dtype=None, stream=None):
+    """One ReplaySSM output-only decode step; returns y.
+
+    Rings: x_ring [slots, H, L, P] (io dtype), dt_ring [slots, H, L] float32,
+    B_ring [slots, G, L, N] (io dtype).  Cursors: write_pos int32 [batch],
+    is_flush uint8 [batch]; the next cursors are written to next_write_pos /
+    next_is_flush when given.
+    """
+    dev = _need(state, "state").device
+    ns, H, P, N = state.shape
+    _need(x, "x", (torch.float32, torch.bfloat16), dev=dev)
+    nb = x.shape[0]
+    io = x.dtype
+    _need(x, "x", io, (nb, H, P))
+    _need(B, "B", io, dev=dev)
+    G = B.shape[1]
+    _need(x_ring, "x_ring", io, dev=dev)
+    L = x_ring.shape[2]
+    _need(x_ring, "x_ring", io, (ns, H, L, P))
+    _need(dt_ring, "dt_ring", torch.float32, (ns, H, L), dev=dev)
+    _need(B_ring, "B_ring", io, (ns, G, L, N), dev=dev)
+    _need(B, "B", io, (nb, G, N))
+    _need(C, "C", io, (nb, G, N))
+    _need(dt, "dt", io, (nb, H))
+    _need(A, "A", torch.float32, (H,))
+    _need(slot_idx, "slot_idx", torch.int32, (nb,))
+    _need(write_pos, "write_pos", torch.int32, (nb,))
+    _need(is_flush, "is_flush", torch.uint8, (nb,))
+    _opt(next_write_pos, "next_write_pos", torch.int32, (nb,))
+    _opt(next_is_flush, "next_is_flush", torch.uint8, (nb,))
+    _opt(D, "D", torch.float32, (H,))
+    _opt(z, "z", io, (nb, H, P))
+    _opt(dt_bias, "dt_bias", torch.float32, (H,))
+    _opt(status, "status", torch.int32, (1,))
+    if y is None:
+        y = torch.empty((nb, H, P), dtype=out_dtype or io, device=dev)
+    _need(y, "y", (torch.float32, torch.bfloat16), (nb, H, P), dev=dev)
+    d = _mamba2_dims(state, x, B, L, y.dtype, dt_softplus)
+    rc = load().replayssm_decode(
+        ctypes.byref(d), _ptr(state), _ptr(x_ring), _ptr(dt_ring), _ptr(B_ring),
+        _ptr(slot_idx), _ptr(write_pos), _ptr(is_flush), _ptr(next_write_pos),
+        _ptr(next_is_flush), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+        _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(y), _ptr(status), _stream(stream))
+    _check("replayssm_decode", rc)
+    return y
+
+
+def replayssm_ring_reset(write_pos, is_flush, rows, ring_len, status=None,
+                         stream=None):
+    """Restart the rings of ``rows`` (int32 device tensor of batch rows)."""
+    dev = _need(write_pos, "write_pos", torch.int32).device
+    nb = write_pos.shape[0]
+    _need(is_flush, "is_flush", torch.uint8, (nb,), dev=dev)
+    _need(rows, "rows", torch.int32, dev=dev)
+    _opt(status, "status", torch.int32, (1,))
+    d = Dims(nb, 1, 0, 0, 1, ring_len, 1, 0, 0, 0, 0)
+    rc = load().replayssm_ring_reset(
+        ctypes.byref(d), _ptr(write_pos), _ptr(is_flush), _ptr(rows),
+        ctypes.c_int32(rows.numel()), _ptr(status), _stream(stream))
+    _check("replayssm_ring_reset", rc)
+
+
+def _gdn_dims(state, q, v, ring_len, o_dtype, scale):
+    ns, HV, V, K = state.shape
+    return GdnDims(v.shape[0], q.shape[1], HV, K, V, ring_len, ns,
+                   _DT[state.dtype], _DT[q.dtype], _DT[o_dtype],
+                   0.0 if scale is None else float(scale))
+
+
+def _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev):
+    ns, HV, V, K = state.shape
+    _need(state, "state", torch.float32)
+    _need(q, "q", (torch.float32, torch.bfloat16), dev=dev)
+    nb, HK = q.shape[0], q.shape[1]
+    io = q.dtype
+    _need(q, "q", io, (nb, HK, K))
+    _need(k, "k", io, (nb, HK, K), dev=dev)
+    _need(v, "v", io, (nb, HV, V), dev=dev)
+    _need(g, "g", torch.float32, (nb, HV), dev=dev)
+    _need(beta, "beta", torch.float32, (nb, HV), dev=dev)
+    if o is None:
+        o = torch.empty((nb, HV, V), dtype=out_dtype or io, device=dev)
+    _need(o, "o", (torch.float32, torch.bfloat16), (nb, HV, V), dev=dev)
+    return nb, HK, o
+
+
+def gdn_standard_decode(state, slot_idx, q, k, v, g, beta, o=None, scale=None,
+                        status=None, out_dtype=None, stream=None):
+    """Recurrent gated-delta-rule step (reads and writes ``state``); returns o."""
+    dev = _need(state, "state").device
+    nb, HK, o = _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev)
+    _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
+    _opt(status, "status", torch.int32, (1,))
+    d = _gdn_dims(state, q, v, 1, o.dtype, scale)
+    rc = load().gdn_standard_decode(
+        ctypes.byref(d), _ptr(state), _ptr(slot_idx), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(g), _ptr(beta), _ptr(o), _ptr(status), _stream(stream))
+    _check("gdn_standard_decode", rc)
+    return o
+
+
+def replayssm_gdn_decode(state, d_ring, k_ring, g_ring, slot_idx, write_pos,
+                         is_flush, q, k, v, g, beta, o=None, next_write_pos=None,
+                         next_is_flush=None, scale=None, status=None,
+                         out_dtype=None, stream=None):
+    """One GDN ReplaySSM decode step; returns o.
+
+    Rings: d_ring [slots, HV, L, V] float32, k_ring [slots, HK, L, K] (io
+    dtype), g_ring [slots, HV, L] float32.
+    """
+    dev = _need(state, "state").device
+    ns, HV, V, K = state.shape
+    nb, HK, o = _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev)
+    _need(d_ring, "d_ring", torch.float32, dev=dev)
+    L = d_ring.shape[2]
+    _need(d_ring, "d_ring", torch.float32, (ns, HV, L, V))
+    _need(k_ring, "k_ring", q.dtype, (ns, HK, L, K), dev=dev)
+    _need(g_ring, "g_ring", torch.float32, (ns, HV, L), dev=dev)
+    _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
+    _need(write_pos, "write_pos", torch.int32, (nb,), dev=dev)
+    _need(is_flush, "is_flush", torch.uint8, (nb,), dev=dev)
+    _opt(next_write_pos, "next_write_pos", torch.int32, (nb,), dev=dev)
+    _opt(next_is_flush, "next_is_flush", torch.uint8, (nb,), dev=dev)
+    _opt(status, "status", torch.int32, (1,))
+    d = _gdn_dims(state, q, v, L, o.dtype, scale)
+    rc = load().replayssm_gdn_decode(
+        ctypes.byref(d), _ptr(state), _ptr(d_ring), _ptr(k_ring), _ptr(g_ring),
+        _ptr(slot_idx), _ptr(write_pos), _ptr(is_flush), _ptr(next_write_pos),
+        _ptr(next_is_flush), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(o), _ptr(status), _stream(stream))
+    _check("replayssm_gdn_decode", rc)
+    return o

@@ -1,0 +1,240 @@
+// Device helpers shared by the decode kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm {
+
+// Raw 16-byte vector: the unit of every coalesced global load and store.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// bf16 storage is carried as its 16-bit pattern.
+struct bf16 {
+  uint16_t bits;
+};
+
+template <typename T> struct Elt;
+
+template <> struct Elt<float> {
+  static constexpr int kPer16 = 4;  // elements per 16-byte vector
+  __device__ static inline void unpack(const u32x4& v, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) f[k] = __uint_as_float(v[k]);
+  }
+  __device__ static inline u32x4 pack(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __float_as_uint(f[k]);
+    return v;
+  }
+  __device__ static inline float load1(const void* p, long i) {
+    return static_cast<const float*>(p)[i];
+  }
+  __device__ static inline void store1(void* p, long i, float f) {
+    static_cast<float*>(p)[i] = f;
+  }
+};
+
+// fp32 -> bf16 rounds to nearest even: clang lowers the __bf16 conversion to
+// the gfx950 hardware convert, which rounds per the default (RNE) mode.
+__device__ static inline uint32_t bf16_pair(float lo, float hi) {
+  const __bf16 a = static_cast<__bf16>(lo);
+  const __bf16 b = static_cast<__bf16>(hi);
+  return uint32_t(__builtin_bit_cast(uint16_t, a)) |
+         (uint32_t(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+template <> struct Elt<bf16> {
+  static constexpr int kPer16 = 8;
+  __device__ static inline void unpack(const u32x4& v, float* f) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      f[2 * k] = __uint_as_float(v[k] << 16);
+      f[2 * k + 1] = __uint_as_float(v[k] & 0xffff0000u);
+    }
+  }
+  __device__ static inline u32x4 pack(const float* f) {
+    u32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = bf16_pair(f[2 * k], f[2 * k + 1]);
+    return v;
+  }
+  __device__ static inline float load1(const void* p, long i) {
+    return __uint_as_float(uint32_t(static_cast<const uint16_t*>(p)[i]) << 16);
+  }
+  __device__ static inline void store1(void* p, long i, float f) {
+    const __bf16 b = static_cast<__bf16>(f);
+    static_cast<uint16_t*>(p)[i] = __builtin_bit_cast(uint16_t, b);
+  }
+};
+
+__device__ static inline u32x4 ld16(const void* base, long byte_off) {
+  return *reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + byte_off);
+}
+
+// Streamed once per step (no reuse within the step): non-temporal hint.
+__device__ static inline u32x4 ld16_stream(const void* base, long byte_off) {
+  return __builtin_nontemporal_load(
+      reinterpret_cast<const u32x4*>(static_cast<const char*>(base) + byte_off));
+}
+
+__device__ static inline void st16(void* base, long byte_off, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(static_cast<char*>(base) + byte_off) = v;
+}
+
+__device__ static inline void st16_stream(void* base, long byte_off, const u32x4& v) {
+  __builtin_nontemporal_store(
+      v, reinterpret_cast<u32x4*>(static_cast<char*>(base) + byte_off));
+}
+
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64);
+// every lane of the group receives the total.
+template <int W>
+__device__ static inline float group_sum(float v) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Workgroups are handed to the 8 XCDs round-robin by workgroup id.  Remap so
+// that each XCD receives one contiguous range of logical tiles: all heads of
+// a batch row then share one XCD's L2 for the row's inputs and ring.
+__device__ static inline int xcd_tile(int bid, int nblocks) {
+  constexpr int kXcd = 8;
+  const int xcd = bid % kXcd;
+  const int local = bid / kXcd;
+  const int q = nblocks / kXcd;
+  const int r = nblocks % kXcd;
+  return xcd * q + (xcd < r ? xcd : r) + local;
+}
+
+// Value of v held by lane `lane` (uniform index), broadcast to the wave.
+__device__ static inline float lane_value(float v, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Exclusive suffix sum across the wave: lane i receives sum_{j>i} v_j.
+__device__ static inline float wave_suffix_exclusive(float v, int lane) {
+  float r = __shfl_down(v, 1, 64);
+  if (lane == 63) r = 0.f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_down(r, o, 64);
+    if (lane + o < 64) r += t;
+  }
+  return r;
+}
+
+// Exclusive suffix product across the wave: lane i receives prod_{j>i} v_j.
+__device__ static inline float wave_suffix_product_exclusive(float v, int lane) {
+  float r = __shfl_down(v, 1, 64);
+  if (lane == 63) r = 1.f;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float t = __shfl_down(r, o, 64);
+    if (lane + o < 64) r *= t;
+  }
+  return r;
+}
+
+// Row reduction of ITEMS partial sums spread over LPR adjacent lanes, as a
+// butterfly transpose: at each level a lane keeps half of its values and
+// trades the other half with its partner, so log2(LPR) levels move
+// ITEMS-1 values per lane instead of ITEMS*log2(LPR).  Afterwards a lane
+// holds NF = ITEMS >> LV complete row sums (value j is item item(j, lane));
+// when LPR > ITEMS, DUP adjacent lanes hold the same sums.
+template <int ITEMS, int LPR>
+struct RowReduce {
+  static constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+  static constexpr int K = ilog2(LPR);
+  static constexpr int M = ilog2(ITEMS);
+  static constexpr int LV = K < M ? K : M;
+  static constexpr int NF = ITEMS >> LV;
+  static constexpr int DUP = 1 << (K - LV);
+  static_assert((1 << K) == LPR && (1 << M) == ITEMS, "powers of two");
+
+  __device__ static inline void run(float (&v)[ITEMS], int lane) {
+#pragma unroll
+    for (int l = 0; l < LV; ++l) {
+      const int o = LPR >> (l + 1);
+      const int h = (ITEMS >> l) >> 1;
+      const bool up = (lane & o) != 0;
+#pragma unroll
+      for (int j = 0; j < h; ++j) {
+        const float send = up ? v[j] : v[j + h];
+        const float keep = up ? v[j + h] : v[j];
+        v[j] = keep + __shfl_xor(send, o, 64);
+      }
+    }
+#pragma unroll
+    for (int l = LV; l < K; ++l) {
+      const int o = LPR >> (l + 1);
+#pragma unroll
+      for (int j = 0; j < NF; ++j) v[j] += __shfl_xor(v[j], o, 64);
+    }
+  }
+  __device__ static inline int item(int j, int lane) {
+    int it = j;
+#pragma unroll
+    for (int l = 0; l < LV; ++l)
+      if (lane & (LPR >> (l + 1))) it += ITEMS >> (l + 1);
+    return it;
+  }
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory straight into LDS (no VGPRs): lane l
+// of the issuing wave writes lds_wave_base + 16*l.  The base must be uniform
+// across the wave.
+__device__ static inline void dma16(const void* gsrc, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+
+// Raw element reads from LDS, converted to fp32.
+template <typename T> struct LdsRead;
+template <> struct LdsRead<float> {
+  __device__ static inline float one(const char* base, int i) {
+    return reinterpret_cast<const float*>(base)[i];
+  }
+  // CNT consecutive elements starting at element i (i*4 bytes, 16B aligned
+  // when CNT >= 4)
+  template <int CNT>
+  __device__ static inline void seg(const char* base, int i, float* out) {
+    const float* p = reinterpret_cast<const float*>(base) + i;
+#pragma unroll
+    for (int k = 0; k < CNT; ++k) out[k] = p[k];
+  }
+};
+template <> struct LdsRead<bf16> {
+  __device__ static inline float one(const char* base, int i) {
+    return __uint_as_float(uint32_t(reinterpret_cast<const uint16_t*>(base)[i]) << 16);
+  }
+  // CNT consecutive elements from element i; pairs are read as 32-bit words
+  // (i even), a single element as 16 bits.
+  template <int CNT>
+  __device__ static inline void seg(const char* base, int i, float* out) {
+    if constexpr (CNT % 2) {
+#pragma unroll
+      for (int k = 0; k < CNT; ++k) out[k] = one(base, i + k);
+    } else {
+      const uint32_t* p = reinterpret_cast<const uint32_t*>(base + 2 * i);
+#pragma unroll
+      for (int k = 0; k < CNT / 2; ++k) {
+        out[2 * k] = __uint_as_float(p[k] << 16);
+        out[2 * k + 1] = __uint_as_float(p[k] & 0xffff0000u);
+      }
+    }
+  }
+};
+
+__device__ static inline float softplus_f32(float v) {
+  return v > 20.f ? v : log1pf(expf(v));
+}
+
+__device__ static inline float silu_gate(float y, float z) {
+  return y * (z / (1.f + expf(-z)));
+}
+
+}  // namespace rssm

@@ -1,0 +1,247 @@
+"""GPU parity of the Mamba2 kernels (standard update and ReplaySSM decode)
+against the float64 oracle, through the C ABI.
+
+Tolerances: fp32 inputs and state -> normwise relative 2e-5 per step and
+tensor; bf16 inputs or state -> 1e-2 absolute (per element, at least one
+bf16 ulp of the reference when y itself is bf16); cursors and ring copies
+bit-exact.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from harness import Tol, log, run_mamba2
+from oracle import mamba2 as OM
+from workloads import (GROUPED, GROUPED_RINGS, LARGE_BATCH, LAYER_2P7B, TINY,
+                       Mamba2Inputs, Mamba2Workload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import linear_recurrence_amd as R
+    R.load()
+
+
+def test_one_hip_runtime_in_process():
+    """The library binds to the HIP runtime torch loaded (one copy mapped)."""
+    import linear_recurrence_amd as R
+    R.load()
+    torch.zeros(1, device="cuda")
+    maps = open("/proc/self/maps").read()
+    libs = {line.split()[-1] for line in maps.splitlines() if "libamdhip64" in line}
+    log(f"hip runtimes mapped: {sorted(libs)}")
+    assert len(libs) == 1
+    assert any("libreplayssm.so" in line for line in maps.splitlines())
+
+
+def test_tiny_all_rows_all_steps():
+    """4 rows, 8 heads, headdim 64, dstate 16, L=4, 32 steps, all fp32."""
+    run_mamba2(TINY, sample=range(TINY.batch))
+
+
+@pytest.mark.parametrize("state_dt,io_dt,out_dt", [
+    (s, i, o) for s in ("f32", "bf16") for i in ("f32", "bf16")
+    for o in (torch.float32, torch.bfloat16)])
+def test_dtype_combinations_ragged(state_dt, io_dt, out_dt):
+    """Every dtype combination on a ragged shape: 5 rows, 6 heads in 3 groups."""
+    wl = Mamba2Workload(f"ragged_{state_dt}_{io_dt}", 5, 6, 64, 32, 3, 4, 13, 11,
+                        io_dt, state_dt, 2000, desync=True)
+    run_mamba2(wl, sample=range(5), y_dtype=out_dt)
+
+
+@pytest.mark.parametrize("P", [32, 64, 128])
+@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
+def test_every_supported_tile_shape(P, N):
+    wl = Mamba2Workload(f"shape_p{P}_n{N}", 3, 2, P, N, 1, 3, 7, 6, "f32", "f32",
+                        2100 + P + N, desync=True)
+    run_mamba2(wl, sample=range(3))
+
+
+def test_layer_2p7b_full_size():
+    """64 rows, 80 heads, dstate 128, L=16, bf16 io, fp32 pool of 1024 slots,
+    256 steps; every row's cursors checked, 8 rows against the oracle."""
+    run_mamba2(LAYER_2P7B, sample=[0, 9, 17, 30, 41, 50, 58, 63])
+
+
+def _large_batch_sample():
+    w0 = Mamba2Inputs(LARGE_BATCH).start_positions().numpy()
+    rows = []
+    for res in range(LARGE_BATCH.ring_len):       # one row per start position
+        rows.append(int(np.nonzero(w0 == res)[0][0]))
+    return rows
+
+
+def test_large_batch_full_size_bench_configuration():
+    """512 rows, bf16 state and io, start positions uniform in [0, 16) so that
+    flush rows interleave every step, 128 steps; bf16 y as the bench runs it."""
+    run_mamba2(LARGE_BATCH, sample=_large_batch_sample(), y_dtype=torch.bfloat16)
+
+
+def test_large_batch_full_size_fp32_output():
+    run_mamba2(LARGE_BATCH, sample=_large_batch_sample()[::3], y_dtype=torch.float32,
+               standard=False)
+
+
+@pytest.mark.parametrize("L", GROUPED_RINGS)
+def test_grouped_with_resets_full_size(L):
+    """256 rows, 128 heads in 8 groups, fp32 pool, 192 steps, slot reuse at
+    steps 37, 101 and 150 (fresh checkpoint, cursors reset mid-ring, stale ring
+    entries poisoned)."""
+    wl = GROUPED.with_ring(L)
+    gen = Mamba2Inputs(wl)
+    reset_rows = sorted({r for t in wl.reset_steps for r in gen.resets(t)[0]})
+    sample = sorted(set(reset_rows[:4] + [1, 128, 255]))
+    run_mamba2(wl, sample=sample, check_every=3)
+
+
+def _small(dev, L=1, state_dt=torch.float32, io=torch.bfloat16, nb=6, H=4, P=64, N=128):
+    g = torch.Generator().manual_seed(7)
+    ns = nb + 3
+    d = dict(
+        state=(torch.randn(ns, H, P, N, generator=g) * 0.1).to(state_dt).to(dev),
+        x=torch.randn(nb, H, P, generator=g).to(io).to(dev),
+        z=torch.randn(nb, H, P, generator=g).to(io).to(dev),
+        dt=torch.randn(nb, H, generator=g).to(io).to(dev),
+        B=(torch.randn(nb, 1, N, generator=g) / 4).to(io).to(dev),
+        C=(torch.randn(nb, 1, N, generator=g) / 4).to(io).to(dev),
+        A=-torch.rand(H, generator=g).add(0.5).to(dev),
+        D=torch.randn(H, generator=g).to(dev),
+        dt_bias=torch.randn(H, generator=g).sub(3).to(dev),
+        slot=torch.randperm(ns, generator=g)[:nb].int().to(dev),
+    )
+    d["x_ring"] = torch.zeros(ns, H, L, P, dtype=io, device=dev)
+    d["dt_ring"] = torch.zeros(ns, H, L, device=dev)
+    d["B_ring"] = torch.zeros(ns, 1, L, N, dtype=io, device=dev)
+    return d
+
+
+@pytest.mark.parametrize("state_dt", [torch.float32, torch.bfloat16])
+def test_L1_replay_is_the_standard_update_bit_for_bit(state_dt):
+    import linear_recurrence_amd as R
+    dev = torch.device("cuda")
+    d = _small(dev, L=1, state_dt=state_dt)
+    s2 = d["state"].clone()
+    wp = torch.zeros(6, dtype=torch.int32, device=dev)
+    fl = torch.ones(6, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        y1 = R.replayssm_decode(d["state"], d["x_ring"], d["dt_ring"], d["B_ring"], d["slot"],
+                                wp, fl, d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"],
+                                z=d["z"], dt_bias=d["dt_bias"], out_dtype=torch.float32)
+        y2 = R.ssu_standard_decode(s2, d["slot"], d["x"], d["dt"], d["A"], d["B"], d["C"],
+                                   D=d["D"], z=d["z"], dt_bias=d["dt_bias"],
+                                   out_dtype=torch.float32)
+        assert torch.equal(y1, y2)
+        assert torch.equal(d["state"].view(torch.int16) if state_dt == torch.bfloat16
+                           else d["state"].view(torch.int32),
+                           s2.view(torch.int16) if state_dt == torch.bfloat16
+                           else s2.view(torch.int32))
+
+
+def test_optional_operands_and_no_softplus():
+    """D, z, dt_bias absent and dt used as given: compared with the oracle."""
+    import linear_recurrence_amd as R
+    dev = torch.device("cuda")
+    d = _small(dev, L=4, io=torch.float32)
+    pool = d["state"].double().cpu().numpy()
+    wp = torch.zeros(6, dtype=torch.int32, device=dev)
+    fl = torch.zeros(6, dtype=torch.uint8, device=dev)
+    nwp, nfl = torch.empty_like(wp), torch.empty_like(fl)
+    dtp = d["dt"].abs() * 0.1
+    o_xr = np.zeros((9, 4, 4, 64))
+    o_dr = np.zeros((9, 4, 4))
+    o_br = np.zeros((9, 1, 4, 128))
+    o_wp, o_fl = np.zeros(6, np.int32), np.zeros(6, np.uint8)
+    for t in range(6):
+        y = R.replayssm_decode(d["state"], d["x_ring"], d["dt_ring"], d["B_ring"], d["slot"],
+                               wp, fl, d["x"], dtp, d["A"], d["B"], d["C"],
+                               next_write_pos=nwp, next_is_flush=nfl, dt_softplus=False,
+                               out_dtype=torch.float32)
+        wp, nwp, fl, nfl = nwp, wp, nfl, fl
+        y_ref, o_wp, o_fl, _ = OM.replay_step(
+            pool, o_xr, o_dr, o_br, d["slot"].cpu().numpy(), o_wp, o_fl,
+            d["x"].double().cpu().numpy(), dtp.double().cpu().numpy(),
+            d["A"].double().cpu().numpy(), d["B"].double().cpu().numpy(),
+            d["C"].double().cpu().numpy(), dt_softplus=False, state_dtype="f32")
+        Tol("rel", 2e-5).check(f"step {t}", y.double().cpu().numpy(), y_ref)
+        assert np.array_equal(wp.cpu().numpy(), o_wp)
+
+
+def test_status_bits_and_safe_handling():
+    """Out-of-contract metadata (forced from the host) sets the status bits;
+    the kernel's own bounds handling keeps every access in range, and rows
+    within the contract are unaffected."""
+    import linear_recurrence_amd as R
+    dev = torch.device("cuda")
+    d = _small(dev, L=4)
+    slot = d["slot"].clone()
+    slot[1] = 10_000                 # outside the pool
+    slot[2] = -3
+    wp = torch.tensor([0, 0, 0, 9, 3, -1], dtype=torch.int32, device=dev)
+    fl = torch.tensor([0, 0, 0, 0, 0, 0], dtype=torch.uint8, device=dev)
+    nwp = torch.full_like(wp, 77)
+    nfl = torch.full_like(fl, 77)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    y = R.replayssm_decode(d["state"], d["x_ring"], d["dt_ring"], d["B_ring"], slot, wp, fl,
+                           d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"], z=d["z"],
+                           dt_bias=d["dt_bias"], next_write_pos=nwp, next_is_flush=nfl,
+                           status=status, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    st = int(status.item())
+    assert st == R.ST_BAD_SLOT | R.ST_BAD_WRITE_POS | R.ST_RING_OVERFLOW
+    assert torch.isnan(y[1]).all() and torch.isnan(y[2]).all()
+    assert torch.isfinite(y[[0, 3, 4, 5]]).all()
+    assert nwp.tolist() == [1, 0, 0, 0, 0, 0]
+    assert nfl.tolist() == [0, 0, 0, 0, 0, 0]
+    # ring reset with a row out of range
+    status.zero_()
+    R.replayssm_ring_reset(nwp, nfl, torch.tensor([0, 99], dtype=torch.int32, device=dev), 4,
+                           status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == R.ST_BAD_ROW and nwp[0].item() == 0
+
+
+def test_empty_batch_is_a_no_op():
+    import linear_recurrence_amd as R
+    dev = torch.device("cuda")
+    d = _small(dev, L=4, nb=6)
+    e = lambda *s, dt=torch.bfloat16: torch.empty(*s, dtype=dt, device=dev)
+    before = d["state"].clone()
+    y = R.replayssm_decode(d["state"], d["x_ring"], d["dt_ring"], d["B_ring"],
+                           e(0, dt=torch.int32), e(0, dt=torch.int32), e(0, dt=torch.uint8),
+                           e(0, 4, 64), e(0, 4), d["A"], e(0, 1, 128), e(0, 1, 128))
+    y2 = R.ssu_standard_decode(d["state"], e(0, dt=torch.int32), e(0, 4, 64), e(0, 4), d["A"],
+                               e(0, 1, 128), e(0, 1, 128))
+    R.replayssm_ring_reset(e(0, dt=torch.int32), e(0, dt=torch.uint8), e(0, dt=torch.int32), 4)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 4, 64) and y2.shape == (0, 4, 64)
+    assert torch.equal(before, d["state"])
+
+
+def test_output_only_rows_never_write_the_pool():
+    """Non-flush rows read S0 and leave every pool byte unchanged; pool slots
+    no row uses stay NaN."""
+    import linear_recurrence_amd as R
+    dev = torch.device("cuda")
+    d = _small(dev, L=8)
+    used = d["slot"].long()
+    unused = torch.tensor(sorted(set(range(9)) - set(used.tolist())), device=dev)
+    d["state"][unused] = float("nan")
+    before = d["state"].clone()
+    wp = torch.zeros(6, dtype=torch.int32, device=dev)
+    fl = torch.zeros(6, dtype=torch.uint8, device=dev)
+    nwp, nfl = torch.empty_like(wp), torch.empty_like(fl)
+    for _ in range(6):                          # 6 < L-1: no flush yet
+        R.replayssm_decode(d["state"], d["x_ring"], d["dt_ring"], d["B_ring"], d["slot"],
+                           wp, fl, d["x"], d["dt"], d["A"], d["B"], d["C"], D=d["D"],
+                           z=d["z"], dt_bias=d["dt_bias"], next_write_pos=nwp,
+                           next_is_flush=nfl)
+        wp, nwp, fl, nfl = nwp, wp, nfl, fl
+    torch.cuda.synchronize()
+    assert torch.equal(before[used], d["state"][used])
+    assert torch.isnan(d["state"][unused]).all()
+    assert wp.tolist() == [6] * 6 and fl.tolist() == [0] * 6

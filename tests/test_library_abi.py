@@ -1,0 +1,77 @@
+"""CPU-side checks of the C-ABI library: it loads and exports every entry
+point declared in include/*.h (no compute calls: there is no GPU here)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", src, re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
+               "gdn_standard_decode", "replayssm_gdn_decode"):
+        assert fn in names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    import linear_recurrence_amd as R
+    if not os.path.exists(R.library_path()):
+        pytest.fail("libreplayssm.so is not built; run __graft_entry__.build()")
+    lib = R.load()
+    for fn in sorted(_declared()):
+        assert hasattr(lib, fn), f"{fn} is declared but not exported"
+    assert set(R.EXPORTS) <= _declared()
+    assert lib.replayssm_abi_version() == 100
+    assert lib.replayssm_strerror(-4).decode().startswith("shape")
+
+
+def test_host_validation_rejects_bad_arguments_without_a_gpu():
+    """Argument checks happen on the host before any HIP call, so they can be
+    exercised here: NULL dims, bad sizes, bad dtypes, unsupported shapes and
+    misaligned pointers all return their codes."""
+    import linear_recurrence_amd as R
+    lib = R.load()
+    V = ctypes.c_void_p
+    good = dict(batch=2, nheads=4, headdim=64, dstate=16, ngroups=2, ring_len=4,
+                num_slots=4, state_dtype=0, io_dtype=0, out_dtype=0, dt_softplus=1)
+
+    def call(**over):
+        d = R.Dims(**{**good, **over.pop("dims", {})})
+        p = {k: V(0x1000) for k in ("state", "xr", "dr", "br", "slot", "wp", "fl",
+                                    "x", "dt", "A", "B", "C", "y")}
+        p.update(over)
+        return lib.replayssm_decode(
+            ctypes.byref(d), p["state"], p["xr"], p["dr"], p["br"], p["slot"],
+            p["wp"], p["fl"], None, None, p["x"], p["dt"], p["A"], p["B"], p["C"],
+            None, None, None, p["y"], None, None)
+
+    assert lib.replayssm_decode(None, *([None] * 20)) == -1
+    assert call(dims=dict(ngroups=3)) == -1
+    assert call(dims=dict(batch=-1)) == -1
+    assert call(dims=dict(io_dtype=5)) == -2
+    assert call(dims=dict(headdim=48)) == -4
+    assert call(dims=dict(ring_len=0)) == -4
+    assert call(dims=dict(ring_len=65)) == -4
+    assert call(x=V(0x1004)) == -1                  # misaligned vector operand
+    assert call(y=None) == -1                       # required pointer
+    assert call(dims=dict(batch=0)) == 0            # empty batch: nothing to do
+    gd = R.GdnDims(2, 1, 2, 128, 128, 4, 4, 1, 1, 1, 0.0)
+    assert lib.gdn_standard_decode(ctypes.byref(gd), *([V(0x1000)] * 8), None, None) == -2
+    d = R.Dims(**good)
+    assert lib.replayssm_ring_reset(ctypes.byref(d), None, None, None, 0, None, None) == 0
+    assert lib.replayssm_ring_reset(ctypes.byref(d), None, None, None, -1, None, None) == -1
