@@ -80,8 +80,8 @@ struct Stage {
   static constexpr int XV = P / IV;  // chunks per x row
   static constexpr int BV = N / IV;  // chunks per B / C row
   static_assert(P % IV == 0 && N % IV == 0, "rows are whole chunks");
-  // ring rows are allocated in multiples of 4 (the dot-product passes)
-  static constexpr int chunks(int L) { return BV + XV + ((L + 3) & ~3) * (XV + BV); }
+  // ring rows are allocated in multiples of 8 (the dot-product passes)
+  static constexpr int chunks(int L) { return BV + XV + ((L + 7) & ~7) * (XV + BV); }
 };
 
 template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY>
@@ -212,7 +212,7 @@ __global__ void __launch_bounds__((TileShape<ST, P, N>::NT))
   }
 
   // ---- 3. decay weights: wt_i = dt_i * exp(A * sum_{i<j<=w} dt_j)
-  const float rsuf = wave_suffix_exclusive(dti, lane);
+  const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
   const float cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
   const float wt = lane <= w ? dti * expf(Ah * rsuf) : 0.f;
 
@@ -224,24 +224,25 @@ __global__ void __launch_bounds__((TileShape<ST, P, N>::NT))
   float part[ITEMS];
   float coef = 0.f;  // lane i: wt_i * (B_i . C) on output-only rows
   if (!f) {
-    // ---- 4a. B_i . C, 16 lanes per dot, 4 dots per pass
-    constexpr int EPL = N / 16;
-    const int q16 = lane & 15;
+    // ---- 4a. B_i . C: 8 lanes per dot, 8 dots per pass
+    constexpr int EPL = N / 8;
+    const int q8 = lane & 7;
     float cpart[EPL];
-    LdsRead<IT>::template seg<EPL>(Cs, q16 * EPL, cpart);
+    LdsRead<IT>::template seg<EPL>(Cs, q8 * EPL, cpart);
     float bc = 0.f;
-    for (int q = 0; q <= (w >> 2); ++q) {
-      const int i = q * 4 + (lane >> 4);
+#pragma unroll 2
+    for (int q = 0; q * 8 <= w; ++q) {
+      const int i = q * 8 + (lane >> 3);
       float bv[EPL];
-      LdsRead<IT>::template seg<EPL>(Bs, i * N + q16 * EPL, bv);
+      LdsRead<IT>::template seg<EPL>(Bs, i * N + q8 * EPL, bv);
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) acc = fmaf(bv[e], cpart[e], acc);
-      acc = group_sum<16>(acc);
-      const float t = __shfl(acc, (lane & 3) * 16, 64);
-      if ((lane >> 2) == q) bc = t;
+      acc = group_sum<8>(acc);
+      const float t = __shfl(acc, (lane & 7) * 8, 64);
+      if ((lane >> 3) == q) bc = t;
     }
-    coef = wt * bc;
+    coef = lane <= w ? wt * bc : 0.f;
     // ---- 5a. S0 @ C per state row
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
@@ -265,16 +266,23 @@ __global__ void __launch_bounds__((TileShape<ST, P, N>::NT))
 #pragma unroll
         for (int j = 0; j < SV; ++j) sf[q][j] *= cumdecay;
       }
-      for (int i = 0; i <= w; ++i) {
-        const float wi = lane_value(wt, i);
-        float bseg[SV];
-        LdsRead<IT>::template seg<SV>(Bs, i * N + c * SV, bseg);
+      // entries in groups of 4; past w the weight is 0 and the row index is
+      // clamped to w, so the extra terms add exact zeros
+      for (int ib = 0; ib <= w; ib += 4) {
 #pragma unroll
-        for (int q = 0; q < IC; ++q) {
-          const int p = (i0 + q) * RPI + prow;
-          const float cf = wi * LdsRead<IT>::one(xs, i * P + p);
+        for (int k = 0; k < 4; ++k) {
+          const int i = ib + k;
+          const int ic = i <= w ? i : w;
+          const float wi = lane_value(wt, i);
+          float bseg[SV];
+          LdsRead<IT>::template seg<SV>(Bs, ic * N + c * SV, bseg);
 #pragma unroll
-          for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(cf, bseg[j], sf[q][j]);
+          for (int q = 0; q < IC; ++q) {
+            const int p = (i0 + q) * RPI + prow;
+            const float cf = wi * LdsRead<IT>::one(xs, ic * P + p);
+#pragma unroll
+            for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(cf, bseg[j], sf[q][j]);
+          }
         }
       }
 #pragma unroll
@@ -298,8 +306,13 @@ __global__ void __launch_bounds__((TileShape<ST, P, N>::NT))
     const int p = RR::item(j, tid) * RPI + prow;
     float yv = part[j];
     if (!f) {
+      // coef is 0 past w; row indexes are clamped to w
       yv *= cumdecay;
-      for (int i = 0; i <= w; ++i) yv = fmaf(lane_value(coef, i), LdsRead<IT>::one(xs, i * P + p), yv);
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        yv = fmaf(lane_value(coef, i), LdsRead<IT>::one(xs, (i <= w ? i : w) * P + p), yv);
+      for (int i = 16; i <= w; ++i)
+        yv = fmaf(lane_value(coef, i), LdsRead<IT>::one(xs, i * P + p), yv);
     }
     yv = fmaf(Dh, LdsRead<IT>::one(xs, w * P + p), yv);
     if (a.z) yv = silu_gate(yv, LdsRead<IT>::one(zs, p));

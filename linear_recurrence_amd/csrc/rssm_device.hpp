@@ -126,6 +126,25 @@ __device__ static inline float wave_suffix_exclusive(float v, int lane) {
   return r;
 }
 
+// Row shift within rows of 16 lanes (DPP): lane i receives lane i+K of its
+// row, 0 past the end of the row.
+template <int K>
+__device__ static inline float row_shl(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x100 + K, 0xF, 0xF, true));
+}
+
+// Exclusive suffix sum over lanes 0..15 (values in lanes > 15 ignored):
+// lane i < 16 receives sum_{i<j<16} v_j.  Five DPP adds.
+__device__ static inline float row16_suffix_exclusive(float v) {
+  float r = row_shl<1>(v);
+  r += row_shl<1>(r);
+  r += row_shl<2>(r);
+  r += row_shl<4>(r);
+  r += row_shl<8>(r);
+  return r;
+}
+
 // Exclusive suffix product across the wave: lane i receives prod_{j>i} v_j.
 __device__ static inline float wave_suffix_product_exclusive(float v, int lane) {
   float r = __shfl_down(v, 1, 64);
@@ -154,11 +173,12 @@ struct RowReduce {
   static constexpr int DUP = 1 << (K - LV);
   static_assert((1 << K) == LPR && (1 << M) == ITEMS, "powers of two");
 
-  __device__ static inline void run(float (&v)[ITEMS], int lane) {
-#pragma unroll
-    for (int l = 0; l < LV; ++l) {
-      const int o = LPR >> (l + 1);
-      const int h = (ITEMS >> l) >> 1;
+  // One level per template instance, so every array index is a constant.
+  template <int L>
+  __device__ static inline void level(float (&v)[ITEMS], int lane) {
+    if constexpr (L < LV) {
+      constexpr int o = LPR >> (L + 1);
+      constexpr int h = (ITEMS >> L) >> 1;
       const bool up = (lane & o) != 0;
 #pragma unroll
       for (int j = 0; j < h; ++j) {
@@ -166,14 +186,15 @@ struct RowReduce {
         const float keep = up ? v[j + h] : v[j];
         v[j] = keep + __shfl_xor(send, o, 64);
       }
-    }
-#pragma unroll
-    for (int l = LV; l < K; ++l) {
-      const int o = LPR >> (l + 1);
+      level<L + 1>(v, lane);
+    } else if constexpr (L < K) {
+      constexpr int o = LPR >> (L + 1);
 #pragma unroll
       for (int j = 0; j < NF; ++j) v[j] += __shfl_xor(v[j], o, 64);
+      level<L + 1>(v, lane);
     }
   }
+  __device__ static inline void run(float (&v)[ITEMS], int lane) { level<0>(v, lane); }
   __device__ static inline int item(int j, int lane) {
     int it = j;
 #pragma unroll
