@@ -59,18 +59,27 @@ struct Mamba2Args {
   int32_t dt_softplus;
 };
 
-// Tile geometry: 16 state vectors per lane where the tile allows it.
-template <typename ST, int P, int N>
+// Tile geometry.  The replay kernel streams 16 state vectors per lane where
+// the tile allows it (its per-tile staging is amortised over more bytes);
+// the standard update, which also writes every tile, runs 4 per lane (more
+// waves in flight).
+template <typename ST, int P, int N, bool REPLAY>
 struct TileShape {
   static constexpr int SV = Elt<ST>::kPer16;  // state elements per vector
   static constexpr int LPR = N / SV;          // lanes per state row
   static constexpr int NVEC = P * N / SV;     // vectors per tile
-  static constexpr int NT =
-      NVEC / 16 < 64 ? 64 : (NVEC / 16 > 512 ? 512 : NVEC / 16);  // threads
+  static constexpr int PER = REPLAY ? 16 : 4; // target vectors per lane
+  static constexpr int NT0 = NVEC / PER;
+  static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 512 ? 512 : NT0);  // threads
   static constexpr int ITEMS = NVEC / NT;     // vectors per lane
   static constexpr int RPI = NT / LPR;        // state rows per item
+  // vectors per fold chunk: 32 fp32 accumulators per lane at most
+  static constexpr int ICMAX = 32 / SV;
+  static constexpr int IC = ITEMS < ICMAX ? ITEMS : ICMAX;
+  static constexpr int NCH = ITEMS / IC;            // fold chunks
   static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "a state row must fit one wave");
   static_assert(NT % 64 == 0 && NVEC % NT == 0, "whole waves, whole tile");
+  static_assert(ITEMS % IC == 0, "fold chunking");
 };
 
 // LDS staging: 16-byte chunks [C | z | x rows 0..w | B rows 0..w], raw.
@@ -84,12 +93,151 @@ struct Stage {
   static constexpr int chunks(int L) { return BV + XV + ((L + 7) & ~7) * (XV + BV); }
 };
 
+// Dot product of SV state elements (one 16-byte vector) with the matching C
+// elements held by the lane.  bf16 x bf16 uses the packed dot2 instruction
+// (exact products, fp32 accumulation); otherwise unpack and fma.
+template <typename ST, typename IT, int SV>
+struct RowDot {
+  static constexpr bool kPacked = std::is_same<ST, bf16>::value && std::is_same<IT, bf16>::value;
+  // C held as fp32 (generic) or as packed bf16 pairs
+  float cf[kPacked ? 1 : SV];
+  uint32_t cp[kPacked ? SV / 2 : 1];
+  __device__ inline void load(const char* Cs, int c) {
+    if constexpr (kPacked) {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(Cs + 2 * c * SV);
+#pragma unroll
+      for (int k = 0; k < SV / 2; ++k) cp[k] = q[k];
+    } else {
+      LdsRead<IT>::template seg<SV>(Cs, c * SV, cf);
+    }
+  }
+  __device__ inline float dot(const u32x4& v) const {
+    float d = 0.f;
+    if constexpr (kPacked) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // copy the element out first: a bit cast of an ext-vector element
+        // expression reads element 0 whatever the index
+        const uint32_t sk = v[k];
+        const uint32_t ck = cp[k];
+        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, sk),
+                                            __builtin_bit_cast(bf16x2_t, ck), d, false);
+      }
+    } else {
+      float f[SV];
+      Elt<ST>::unpack(v, f);
+#pragma unroll
+      for (int j = 0; j < SV; ++j) d = fmaf(f[j], cf[j], d);
+    }
+    return d;
+  }
+  // C as fp32, for the fold's dot with the new state
+  __device__ inline void cvals(float* out) const {
+    if constexpr (kPacked) {
+#pragma unroll
+      for (int k = 0; k < SV / 2; ++k) {
+        out[2 * k] = __uint_as_float(cp[k] << 16);
+        out[2 * k + 1] = __uint_as_float(cp[k] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SV; ++j) out[j] = cf[j];
+    }
+  }
+};
+
+// Fold one chunk of IC state vectors: S_new = cumdecay*S0 + sum_i wt_i x_i B_i
+// for the rows and columns this lane holds; store it; write the row partial
+// sums of S_new . C into part[I0 .. I0+IC).
+template <typename ST, typename IT, int P, int N, int NT, int SV, int IC, int RPI, int ITEMS, int I0>
+__device__ __forceinline__ void fold_chunk(const u32x4 (&raw)[IC], float (&part)[ITEMS], int w,
+                                           float wt, float cumdecay, const char* Bs,
+                                           const char* xs, int c, int prow, const float* cv,
+                                           char* tile, uint32_t lane_off) {
+  float sf[IC][SV];
+#pragma unroll
+  for (int q = 0; q < IC; ++q)
+#pragma unroll
+    for (int j = 0; j < SV; ++j) sf[q][j] = 0.f;
+  // entries in groups of 4; past w the weight is 0 and the row index is
+  // clamped to w, so the extra terms add exact zeros
+  for (int ib = 0; ib <= w; ib += 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = ib + k;
+      const int ic = i <= w ? i : w;
+      const float wi = lane_value(wt, i);
+      float bseg[SV];
+      LdsRead<IT>::template seg<SV>(Bs, ic * N + c * SV, bseg);
+#pragma unroll
+      for (int q = 0; q < IC; ++q) {
+        const int p = (I0 + q) * RPI + prow;
+        const float cf = wi * LdsRead<IT>::one(xs, ic * P + p);
+#pragma unroll
+        for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(cf, bseg[j], sf[q][j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < IC; ++q) {
+    float s0[SV];
+    Elt<ST>::unpack(raw[q], s0);
+    float d = 0.f;
+#pragma unroll
+    for (int j = 0; j < SV; ++j) {
+      sf[q][j] = fmaf(cumdecay, s0[j], sf[q][j]);
+      d = fmaf(sf[q][j], cv[j], d);
+    }
+    // keep the row sum here: left alone, the compiler sinks it past the
+    // later chunks and keeps every chunk's accumulators alive until the end
+    asm volatile("" : "+v"(d));
+    part[I0 + q] = d;
+    // Global (not buffer) store: a buffer store with an SGPR offset whose
+    // data registers are rewritten by the next VALU instruction can send the
+    // new value on gfx950, and the compiler only guards the global form.
+    st16_stream(tile, (long)lane_off + (I0 + q) * NT * 16, Elt<ST>::pack(sf[q]));
+  }
+}
+
+struct FoldCtx {
+  int w;
+  float wt, cumdecay;
+  const char* Bs;
+  const char* xs;
+  int c, prow;
+  rsrc_t trs;    // state tile, for the chunk loads
+  char* tile;    // state tile, for the stores
+  uint32_t lane_off;
+};
+
+// Fold chunks CH, CH+1, ... of the tile.  Chunks alternate between the two
+// register buffers; once chunk CH is folded its buffer receives chunk CH+2,
+// so one chunk is always in flight while another is folded.
+template <typename ST, typename IT, int P, int N, int NT, int SV, int IC, int RPI, int ITEMS, int CH>
+__device__ __forceinline__ void fold_from(u32x4 (&ra)[IC], u32x4 (&rb)[IC], float (&part)[ITEMS],
+                                          const float* cv, const FoldCtx& fc) {
+  constexpr int NCH = ITEMS / IC;
+  if constexpr (CH < NCH) {
+    u32x4 (&buf)[IC] = (CH % 2 == 0) ? ra : rb;
+    fold_chunk<ST, IT, P, N, NT, SV, IC, RPI, ITEMS, CH * IC>(buf, part, fc.w, fc.wt, fc.cumdecay,
+                                                             fc.Bs, fc.xs, fc.c, fc.prow, cv,
+                                                             fc.tile, fc.lane_off);
+    if constexpr (CH + 2 < NCH) {
+#pragma unroll
+      for (int q = 0; q < IC; ++q)
+        buf[q] = bload16_nt(fc.trs, fc.lane_off, ((CH + 2) * IC + q) * NT * 16);
+    }
+    fold_from<ST, IT, P, N, NT, SV, IC, RPI, ITEMS, CH + 1>(ra, rb, part, cv, fc);
+  }
+}
+
 template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY>
-__global__ void __launch_bounds__((TileShape<ST, P, N>::NT))
+__global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
     mamba2_decode_kernel(const Mamba2Args a) {
-  using TS = TileShape<ST, P, N>;
+  using TS = TileShape<ST, P, N, REPLAY>;
   using SG = Stage<IT, P, N>;
   constexpr int SV = TS::SV, LPR = TS::LPR, NT = TS::NT, ITEMS = TS::ITEMS, RPI = TS::RPI;
+  constexpr int IC = TS::IC, NCH = TS::NCH;
   constexpr int XV = SG::XV, BV = SG::BV;
   constexpr long kSt = sizeof(ST);
   constexpr long kIo = sizeof(IT);
@@ -140,167 +288,145 @@ __global__ void __launch_bounds__((TileShape<ST, P, N>::NT))
     return;
   }
 
-  // ---- 1. issue every global read of the step
-  const long tile_byte = ((long)s * H + h) * (long)P * N * kSt;
-  u32x4 sv[ITEMS];
-#pragma unroll
-  for (int it = 0; it < ITEMS; ++it)
-    sv[it] = ld16_stream(a.state, tile_byte + ((long)it * NT + tid) * 16);
-
+  char* const tptr = (char*)a.state + ((long)s * H + h) * (long)P * N * kSt;
+  const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(P * N * kSt));
+  const uint32_t lane_off = tid * 16;
   const long xcur = yoff;                                // x[b, h, :]
   const long bccur = ((long)b * a.ngroups + g) * N;      // B, C[b, g, :]
   const long xring0 = ((long)s * H + h) * (long)L * P;   // x_ring[s, h, 0, :]
   const long bring0 = ((long)s * a.ngroups + g) * (long)L * N;
+  const long dtring0 = ((long)s * H + h) * L;
   const int nZ = a.z ? XV : 0;
   const int oX = BV + nZ;                // first chunk of the x rows
   const int oB = oX + (w + 1) * XV;      // first chunk of the B rows
   const int nAll = oB + (w + 1) * BV;
-  for (int k = 0; k * NT < nAll; ++k) {
-    const int u = k * NT + tid;
-    if (u < nAll) {
-      const char* src;
-      if (u < BV) {
-        src = (const char*)a.C + (bccur * kIo + (long)u * 16);
-      } else if (u < oX) {
-        src = (const char*)a.z + (xcur * kIo + (long)(u - BV) * 16);
-      } else if (u < oB) {
-        const int i = (u - oX) / XV, c = (u - oX) - i * XV;
-        src = (REPLAY && i < w) ? (const char*)a.x_ring + ((xring0 + (long)i * P) * kIo + c * 16)
-                                : (const char*)a.x + (xcur * kIo + c * 16);
-      } else {
-        const int i = (u - oB) / BV, c = (u - oB) - i * BV;
-        src = (REPLAY && i < w) ? (const char*)a.B_ring + ((bring0 + (long)i * N) * kIo + c * 16)
-                                : (const char*)a.B + (bccur * kIo + c * 16);
+
+  // Stage C, z, x_0..x_w, B_0..B_w (entry w = the current step) into LDS
+  // with direct-to-LDS loads, and load dt of entries 0..w (lane i).
+  auto stage = [&]() {
+    for (int k = 0; k * NT < nAll; ++k) {
+      const int u = k * NT + tid;
+      if (u < nAll) {
+        const char* src;
+        if (u < BV) {
+          src = (const char*)a.C + (bccur * kIo + (long)u * 16);
+        } else if (u < oX) {
+          src = (const char*)a.z + (xcur * kIo + (long)(u - BV) * 16);
+        } else if (u < oB) {
+          const int i = (u - oX) / XV, cc = (u - oX) - i * XV;
+          src = (REPLAY && i < w)
+                    ? (const char*)a.x_ring + ((xring0 + (long)i * P) * kIo + cc * 16)
+                    : (const char*)a.x + (xcur * kIo + cc * 16);
+        } else {
+          const int i = (u - oB) / BV, cc = (u - oB) - i * BV;
+          src = (REPLAY && i < w)
+                    ? (const char*)a.B_ring + ((bring0 + (long)i * N) * kIo + cc * 16)
+                    : (const char*)a.B + (bccur * kIo + cc * 16);
+        }
+        dma16(src, lds + ((long)k * NT + wave * 64) * 16);
       }
-      dma16(src, lds + ((long)k * NT + wave * 64) * 16);
     }
-  }
-  // dt of entries 0..w: lane i < w from the ring, lane w the current step
-  const long dtring0 = ((long)s * H + h) * L;
+  };
   float dti = 0.f;
   if (REPLAY && lane < w) dti = a.dt_ring[dtring0 + lane];
-  const float Ah = a.A[h];
-  const float Dh = a.D ? a.D[h] : 0.f;
   {
     const float v = Elt<IT>::load1(a.dt, (long)b * H + h) + (a.dt_bias ? a.dt_bias[h] : 0.f);
     const float dcur = a.dt_softplus ? softplus_f32(v) : v;
     if (lane == w) dti = dcur;
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  const float Ah = a.A[h];
+  const float Dh = a.D ? a.D[h] : 0.f;
 
   const char* Cs = lds;
   const char* zs = lds + BV * 16;
   const char* xs = lds + oX * 16;
   const char* Bs = lds + (long)oB * 16;
-
-  // ---- 2. append the current step to the ring (output-only rows)
-  const bool append = REPLAY && !f;
-  if (append && wave == 0) {
-    const bool b_writer = (h % a.hpg) == 0;  // one writer per group
-    for (int k = lane; k < XV + BV; k += 64) {
-      if (k < XV) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(xs + ((long)w * XV + k) * 16);
-        st16(a.x_ring, ((xring0 + (long)w * P) * kIo) + k * 16, v);
-      } else if (b_writer) {
-        const int cb = k - XV;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + ((long)w * BV + cb) * 16);
-        st16(a.B_ring, ((bring0 + (long)w * N) * kIo) + cb * 16, v);
-      }
-    }
-    if (lane == w) a.dt_ring[dtring0 + w] = dti;
-  }
-
-  // ---- 3. decay weights: wt_i = dt_i * exp(A * sum_{i<j<=w} dt_j)
-  const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
-  const float cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
-  const float wt = lane <= w ? dti * expf(Ah * rsuf) : 0.f;
-
-  // C segment of this lane's state columns
   const int c = tid % LPR;
-  float cseg[SV];
-  LdsRead<IT>::template seg<SV>(Cs, c * SV, cseg);
+  const int prow = tid / LPR;
 
   float part[ITEMS];
-  float coef = 0.f;  // lane i: wt_i * (B_i . C) on output-only rows
+  float cumdecay, coef = 0.f;  // coef (lane i): wt_i * (B_i . C), output-only rows
   if (!f) {
-    // ---- 4a. B_i . C: 8 lanes per dot, 8 dots per pass
-    constexpr int EPL = N / 8;
-    const int q8 = lane & 7;
-    float cpart[EPL];
-    LdsRead<IT>::template seg<EPL>(Cs, q8 * EPL, cpart);
-    float bc = 0.f;
-#pragma unroll 2
-    for (int q = 0; q * 8 <= w; ++q) {
-      const int i = q * 8 + (lane >> 3);
-      float bv[EPL];
-      LdsRead<IT>::template seg<EPL>(Bs, i * N + q8 * EPL, bv);
-      float acc = 0.f;
+    // ================= output-only tile: the whole tile in flight at once
+    u32x4 sv[ITEMS];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc = fmaf(bv[e], cpart[e], acc);
-      acc = group_sum<8>(acc);
-      const float t = __shfl(acc, (lane & 7) * 8, 64);
-      if ((lane >> 3) == q) bc = t;
-    }
-    coef = lane <= w ? wt * bc : 0.f;
-    // ---- 5a. S0 @ C per state row
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      float sf[SV];
-      Elt<ST>::unpack(sv[it], sf);
-      float d = 0.f;
-#pragma unroll
-      for (int j = 0; j < SV; ++j) d = fmaf(sf[j], cseg[j], d);
-      part[it] = d;
-    }
-  } else {
-    // ---- 5b. fold: S_new = cumdecay * S0 + sum_i wt_i * outer(x_i, B_i)
-    constexpr int IC = ITEMS < 4 ? ITEMS : 4;  // items folded together
-    const int prow = tid / LPR;
-#pragma unroll
-    for (int i0 = 0; i0 < ITEMS; i0 += IC) {
-      float sf[IC][SV];
-#pragma unroll
-      for (int q = 0; q < IC; ++q) {
-        Elt<ST>::unpack(sv[i0 + q], sf[q]);
-#pragma unroll
-        for (int j = 0; j < SV; ++j) sf[q][j] *= cumdecay;
-      }
-      // entries in groups of 4; past w the weight is 0 and the row index is
-      // clamped to w, so the extra terms add exact zeros
-      for (int ib = 0; ib <= w; ib += 4) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int i = ib + k;
-          const int ic = i <= w ? i : w;
-          const float wi = lane_value(wt, i);
-          float bseg[SV];
-          LdsRead<IT>::template seg<SV>(Bs, ic * N + c * SV, bseg);
-#pragma unroll
-          for (int q = 0; q < IC; ++q) {
-            const int p = (i0 + q) * RPI + prow;
-            const float cf = wi * LdsRead<IT>::one(xs, ic * P + p);
-#pragma unroll
-            for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(cf, bseg[j], sf[q][j]);
-          }
+    for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
+    stage();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    // append the current step at ring position w (replay only: the standard
+    // update has no ring and never reaches this branch)
+    if (REPLAY && wave == 0) {
+      const bool b_writer = (h % a.hpg) == 0;  // one writer per group
+      for (int k = lane; k < XV + BV; k += 64) {
+        if (k < XV) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xs + ((long)w * XV + k) * 16);
+          st16(a.x_ring, ((xring0 + (long)w * P) * kIo) + k * 16, v);
+        } else if (b_writer) {
+          const int cb = k - XV;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + ((long)w * BV + cb) * 16);
+          st16(a.B_ring, ((bring0 + (long)w * N) * kIo) + cb * 16, v);
         }
       }
-#pragma unroll
-      for (int q = 0; q < IC; ++q) {
-        float d = 0.f;
-#pragma unroll
-        for (int j = 0; j < SV; ++j) d = fmaf(sf[q][j], cseg[j], d);
-        part[i0 + q] = d;
-        st16_stream(a.state, tile_byte + ((long)(i0 + q) * NT + tid) * 16, Elt<ST>::pack(sf[q]));
-      }
+      if (lane == w) a.dt_ring[dtring0 + w] = dti;
     }
+    // decay weights: wt_i = dt_i * exp(A * sum_{i<j<=w} dt_j)
+    const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
+    cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
+    const float wt = lane <= w ? dti * expf(Ah * rsuf) : 0.f;
+    // B_i . C: 8 lanes per dot, 8 dots per pass
+    {
+      constexpr int EPL = N / 8;
+      const int q8 = lane & 7;
+      float cpart[EPL];
+      LdsRead<IT>::template seg<EPL>(Cs, q8 * EPL, cpart);
+      float bc = 0.f;
+#pragma unroll 2
+      for (int q = 0; q * 8 <= w; ++q) {
+        const int i = q * 8 + (lane >> 3);
+        float bv[EPL];
+        LdsRead<IT>::template seg<EPL>(Bs, i * N + q8 * EPL, bv);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(bv[e], cpart[e], acc);
+        acc = group_sum<8>(acc);
+        const float t = __shfl(acc, (lane & 7) * 8, 64);
+        if ((lane >> 3) == q) bc = t;
+      }
+      coef = lane <= w ? wt * bc : 0.f;
+    }
+    // S0 . C per state row
+    RowDot<ST, IT, SV> rd;
+    rd.load(Cs, c);
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) part[it] = rd.dot(sv[it]);
+  } else {
+    // ================= flush tile: stream the tile in chunks, fold, store
+    u32x4 ra[IC], rb[IC];
+#pragma unroll
+    for (int q = 0; q < IC; ++q) ra[q] = bload16_nt(trs, lane_off, q * NT * 16);
+    if constexpr (NCH > 1) {
+#pragma unroll
+      for (int q = 0; q < IC; ++q) rb[q] = bload16_nt(trs, lane_off, (IC + q) * NT * 16);
+    }
+    stage();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
+    cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
+    const float wt = lane <= w ? dti * expf(Ah * rsuf) : 0.f;
+    RowDot<ST, IT, SV> rd;
+    rd.load(Cs, c);
+    float cv[SV];
+    rd.cvals(cv);
+    FoldCtx fc{w, wt, cumdecay, Bs, xs, c, prow, trs, tptr, lane_off};
+    fold_from<ST, IT, P, N, NT, SV, IC, RPI, ITEMS, 0>(ra, rb, part, cv, fc);
   }
 
-  // ---- 6. whole rows per lane; reconstruction, D*x, gate, store
+  // ---- whole rows per lane; ring term, D*x, gate, store
   using RR = RowReduce<ITEMS, LPR>;
   RR::run(part, tid);
   const bool writer = (c % RR::DUP) == 0;
-  const int prow = tid / LPR;
 #pragma unroll
   for (int j = 0; j < RR::NF; ++j) {
     const int p = RR::item(j, tid) * RPI + prow;
@@ -322,7 +448,7 @@ __global__ void __launch_bounds__((TileShape<ST, P, N>::NT))
 
 template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY>
 static int launch_mamba2(const Mamba2Args& a, int batch, hipStream_t stream) {
-  using TS = TileShape<ST, P, N>;
+  using TS = TileShape<ST, P, N, REPLAY>;
   const int L = REPLAY ? a.ring_len : 1;  // L <= 64: one dt per lane of a wave
   const size_t lds = (size_t)Stage<IT, P, N>::chunks(L) * 16;
   if (lds > kMaxLds) return RSSM_ESHAPE;  // ring rows must fit one workgroup's LDS

@@ -13,6 +13,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 struct bf16 {
   uint16_t bits;
 };
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Elt;
 
@@ -86,6 +87,22 @@ __device__ static inline void st16(void* base, long byte_off, const u32x4& v) {
 __device__ static inline void st16_stream(void* base, long byte_off, const u32x4& v) {
   __builtin_nontemporal_store(
       v, reinterpret_cast<u32x4*>(static_cast<char*>(base) + byte_off));
+}
+
+// Raw buffer loads from one state tile: the descriptor (uniform base, size
+// in bytes) lives in SGPRs, a lane needs one VGPR offset for all of its
+// vectors and the per-vector offset goes in an SGPR.  Loads at or past
+// `bytes` read 0 (hardware range check).  Word 3 is the gfx9-family value
+// for raw (unformatted) buffers; aux 2 = non-temporal.  Stores stay global:
+// with an SGPR offset, a buffer store's data registers must not be
+// rewritten by the next VALU instruction, a hazard the compiler does not
+// guard for that form.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ static inline rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+__device__ static inline u32x4 bload16_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 2);
 }
 
 // Sum over aligned groups of W consecutive lanes (W a power of two <= 64);
