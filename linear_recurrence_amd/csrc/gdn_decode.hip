@@ -10,12 +10,21 @@
 // snippet of sglang #28695 "[GDN] Support ReplaySSM Ring Spec-Verify".
 // Formulas: see the contract in replayssm.h.
 //
-// Mapping (one workgroup per (row, value head) tile of the [V, K] state):
-// the tile is streamed with 16-byte non-temporal loads into registers; LPR
-// consecutive lanes hold one state row and reduce S0 @ k and S0 @ q over K
-// with xor shuffles.  The ring rows, q, v and the gates are staged in LDS.
-// The contractions here are two matrix-vector products and, on flush rows,
-// a rank-(w+1) update with w+1 <= L: too thin for the matrix cores to pay,
+// Mapping (one workgroup per (row, value head) tile of the [V, K] fp32
+// state; LPR = K/4 adjacent lanes hold one state row):
+//  * every global read of the step is issued at once: the tile into
+//    registers with raw buffer loads, q, v, k_0..k_w and d_0..d_{w-1} into
+//    LDS with direct-to-LDS loads, the gates into lanes;
+//  * gate products by DPP suffix scans, ring dots k_i.k_w and k_i.q on 16
+//    lanes each (packed bf16 dot2 for bf16 inputs), their weights broadcast
+//    through LDS;
+//  * S0.k_w and S0.q per state row by a butterfly transpose-reduce, then
+//    one lane per row forms pred, d_w and o;
+//  * flush rows fold Gamma*S0 + sum_i gamma_i outer(d_i, k_i) in chunks of
+//    the registers, with gamma_i*d_i precomputed in LDS, and store with
+//    global stores.
+// The contractions are two matrix-vector products and, on flush rows, a
+// rank-(w+1) update with w+1 <= L: too thin for the matrix cores to pay,
 // and the kernel is bound by the state stream, so they run on the VALU.
 #include <math.h>
 
@@ -49,44 +58,88 @@ struct GdnArgs {
   float scale;
 };
 
-template <int V, int K>
-__host__ __device__ constexpr int gdn_lds_floats(int L) {
-  return L * K + L * V + K + V + 4 * L + 4;
-}
-
-template <typename IT, typename OT, int V, int K, int NT, bool REPLAY>
-__global__ void __launch_bounds__(NT) gdn_decode_kernel(const GdnArgs a) {
-  constexpr int SV = 4;              // fp32 state elements per vector
-  constexpr int LPR = K / SV;        // lanes per state row
+template <int V, int K, bool REPLAY>
+struct GdnShape {
+  static constexpr int SV = 4;               // fp32 state elements per vector
+  static constexpr int LPR = K / SV;         // lanes per state row
+  static constexpr int NVEC = V * K / SV;
+  static constexpr int PER = REPLAY ? 16 : 8;
+  static constexpr int NT0 = NVEC / PER;
+  static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 1024 ? 1024 : NT0);
+  static constexpr int ITEMS = NVEC / NT;
+  static constexpr int RPI = NT / LPR;
+  static constexpr int IC = ITEMS < 8 ? ITEMS : 8;  // fold chunk: 32 accumulators
   static_assert(LPR <= 64 && 64 % LPR == 0, "a state row must fit one wave");
-  constexpr int NVEC = V * K / SV;
-  static_assert(NT % 64 == 0 && NVEC % NT == 0, "whole waves, whole tile");
-  constexpr int ITEMS = NVEC / NT;
-  constexpr int RPI = NT / LPR;
-  constexpr int IV = Elt<IT>::kPer16;
-  static_assert(K % IV == 0 && V % IV == 0, "rows are whole vectors");
-  constexpr int KV = K / IV;
-  constexpr int VV = V / IV;
+  static_assert(NT % 64 == 0 && NVEC % NT == 0 && ITEMS % IC == 0, "tiling");
+};
+
+// LDS: 16-byte chunks [q | v | k rows (8-row multiples) | d rows 0..L-1 (fp32)]
+template <typename IT, int V, int K>
+struct GdnStage {
+  static constexpr int IV = Elt<IT>::kPer16;
+  static constexpr int QV = K / IV;  // chunks per q / k row
+  static constexpr int VV = V / IV;  // chunks per v row
+  static constexpr int DV = V / 4;   // chunks per d row
+  static_assert(K % IV == 0 && V % IV == 0, "rows are whole chunks");
+  static constexpr int oK = QV + VV;
+  static constexpr int oD(int L) { return oK + ((L + 7) & ~7) * QV; }
+  static constexpr int chunks(int L) { return oD(L) + L * DV; }
+};
+
+// Dot products of a 16-lane share of two bf16/fp32 vectors held in LDS.
+template <typename IT, int EPL>
+struct SegDot {
+  static constexpr bool kPacked = std::is_same<IT, bf16>::value && EPL % 2 == 0;
+  uint32_t pk[kPacked ? EPL / 2 : 1];
+  float fv[kPacked ? 1 : EPL];
+  __device__ inline void load(const char* base, int e0) {
+    if constexpr (kPacked) {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(base + 2 * e0);
+#pragma unroll
+      for (int k = 0; k < EPL / 2; ++k) pk[k] = q[k];
+    } else {
+      LdsRead<IT>::template seg<EPL>(base, e0, fv);
+    }
+  }
+  __device__ inline float dot(const SegDot& o) const {
+    float d = 0.f;
+    if constexpr (kPacked) {
+#pragma unroll
+      for (int k = 0; k < EPL / 2; ++k) {
+        const uint32_t x = pk[k], y = o.pk[k];  // scalars first: see RowDot
+        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x),
+                                            __builtin_bit_cast(bf16x2_t, y), d, false);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) d = fmaf(fv[k], o.fv[k], d);
+    }
+    return d;
+  }
+};
+
+template <typename IT, typename OT, int V, int K, bool REPLAY>
+__global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kernel(const GdnArgs a) {
+  using GS = GdnShape<V, K, REPLAY>;
+  using SG = GdnStage<IT, V, K>;
+  constexpr int SV = GS::SV, LPR = GS::LPR, NT = GS::NT, ITEMS = GS::ITEMS, RPI = GS::RPI;
+  constexpr int IC = GS::IC;
+  constexpr int QV = SG::QV, VV = SG::VV, DV = SG::DV;
   constexpr long kIo = sizeof(IT);
 
-  extern __shared__ __attribute__((aligned(16))) float lds[];
-  const int L = REPLAY ? a.ring_len : 1;
-  float* ks = lds;            // [L][K]  k of entries 0..w
-  float* ds = ks + L * K;     // [L][V]  d of entries 0..w-1, then d_w
-  float* qs = ds + L * V;     // [K]
-  float* vs = qs + K;         // [V]     v of the current step
-  float* gs = vs + V;         // [L]     g of entries 0..w
-  float* gam = gs + L;        // [L]     prod_{i<j<=w} g_j
-  float* kk = gam + L;        // [L]     k_i . k_w
-  float* kq = kk + L;         // [L]     k_i . q
-  float* scal = kq + L;       // [0] = Gamma
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ __attribute__((aligned(16))) float cf_lds[2 * NT];  // per wave: ring weights
+  __shared__ float gm_lds[64];                                   // gamma_i
 
+  const int L = REPLAY ? a.ring_len : 1;
   const int HV = a.v_heads;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
   const int b = tile / HV;
   const int hv = tile - b * HV;
   const int hk = hv / a.vpk;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int s = a.slot_idx[b];
   int w = 0;
@@ -121,122 +174,94 @@ __global__ void __launch_bounds__(NT) gdn_decode_kernel(const GdnArgs a) {
     return;
   }
 
-  // ---- 1. stream S0 = state[s, hv]
-  const long tile_byte = ((long)s * HV + hv) * (long)V * K * 4;
+  // ---- 1. every global read of the step
+  char* const tptr = (char*)a.state + ((long)s * HV + hv) * (long)V * K * 4;
+  const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(V * K * 4));
+  const uint32_t lane_off = tid * 16;
   u32x4 sv[ITEMS];
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it)
-    sv[it] = ld16_stream(a.state, tile_byte + ((long)it * NT + tid) * 16);
+  for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
 
-  // ---- 2. stage q, v, k_0..k_w, d_0..d_{w-1}, g_0..g_w
-  const bool append = REPLAY && !f;
-  const bool k_writer = (hv % a.vpk) == 0;
-  const long qk_cur = ((long)b * a.k_heads + hk) * K;
-  const long kring0 = ((long)s * a.k_heads + hk) * (long)L * K;
-  const long dring0 = ((long)s * HV + hv) * (long)L * V;
+  const long qk_cur = ((long)b * a.k_heads + hk) * K;             // q, k[b, hk, :]
+  const long kring0 = ((long)s * a.k_heads + hk) * (long)L * K;   // k_ring[s, hk, 0, :]
+  const long dring0 = ((long)s * HV + hv) * (long)L * V;          // d_ring[s, hv, 0, :]
   const long gring0 = ((long)s * HV + hv) * L;
-  const int nQ = KV, nV = VV, nK = (w + 1) * KV, nD = w * (V / 4);
-  const int nAll = nQ + nV + nK + nD;
-  for (int u = tid; u < nAll; u += NT) {
-    int c = u;
-    if (c < nQ) {
-      float fv[IV];
-      Elt<IT>::unpack(ld16(a.q, (qk_cur + c * IV) * kIo), fv);
-#pragma unroll
-      for (int j = 0; j < IV; ++j) qs[c * IV + j] = fv[j];
-      continue;
-    }
-    c -= nQ;
-    if (c < nV) {
-      float fv[IV];
-      Elt<IT>::unpack(ld16(a.v, (ooff + c * IV) * kIo), fv);
-#pragma unroll
-      for (int j = 0; j < IV; ++j) vs[c * IV + j] = fv[j];
-      continue;
-    }
-    c -= nV;
-    if (c < nK) {
-      const int i = c / KV;
-      const int cc = c - i * KV;
-      u32x4 raw;
-      if (REPLAY && i < w) {
-        raw = ld16(a.k_ring, (kring0 + (long)i * K + cc * IV) * kIo);
-      } else {
-        raw = ld16(a.k, (qk_cur + cc * IV) * kIo);
-        if (append && k_writer) st16(a.k_ring, (kring0 + (long)w * K + cc * IV) * kIo, raw);
+  const int oK = SG::oK;
+  const int oD = SG::oD(L);
+  auto dma_span = [&](int c0, int n, const char* ring, int nring, const char* cur) {
+    for (int j = wave * 64; j < n; j += NT) {
+      const int u = j + lane;
+      if (u < n) {
+        const char* src = u < nring ? ring + (long)u * 16 : cur + (long)(u - nring) * 16;
+        dma16(src, lds + (long)(c0 + j) * 16);
       }
-      float fv[IV];
-      Elt<IT>::unpack(raw, fv);
-#pragma unroll
-      for (int j = 0; j < IV; ++j) ks[i * K + cc * IV + j] = fv[j];
-      continue;
     }
-    c -= nK;
-    {
-      // d ring rows are fp32: 4 per vector
-      const int i = c / (V / 4);
-      const int cc = c - i * (V / 4);
-      float fv[4];
-      Elt<float>::unpack(ld16(a.d_ring, (dring0 + (long)i * V + cc * 4) * 4), fv);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) ds[i * V + cc * 4 + j] = fv[j];
+  };
+  {
+    const char* qg = (const char*)a.q + qk_cur * kIo;
+    const char* vg = (const char*)a.v + ooff * kIo;
+    dma_span(0, QV, qg, QV, qg);
+    dma_span(QV, VV, vg, VV, vg);
+    dma_span(oK, (w + 1) * QV, REPLAY ? (const char*)a.k_ring + kring0 * kIo : nullptr,
+             REPLAY ? w * QV : 0, (const char*)a.k + qk_cur * kIo);
+    if (REPLAY && w > 0) {
+      const char* dg = (const char*)a.d_ring + dring0 * 4;
+      dma_span(oD, w * DV, dg, w * DV, dg);
     }
   }
   const float gw = a.g[(long)b * HV + hv];
-  for (int i = tid; i <= w; i += NT) {
-    if (REPLAY && i < w) {
-      gs[i] = a.g_ring[gring0 + i];
-    } else {
-      gs[i] = gw;
-      if (append) a.g_ring[gring0 + w] = gw;
-    }
-  }
+  const float bw = a.beta[(long)b * HV + hv];
+  float gl = 1.f;  // g of entry `lane` (1 past w: neutral in products)
+  if (REPLAY && lane < w) gl = a.g_ring[gring0 + lane];
+  if (lane == w) gl = gw;
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // ---- 3. gates and ring dots
-  for (int i = tid; i <= w; i += NT) {
-    float p = 1.f;
-    for (int j = w; j > i; --j) p *= gs[j];
-    gam[i] = p;
-  }
-  if (tid == 0) {
-    float p = 1.f;
-    for (int j = w; j >= 0; --j) p *= gs[j];
-    scal[0] = p;
-  }
+  const char* Qs = lds;
+  const char* Vs = lds + QV * 16;
+  const char* Ks = lds + oK * 16;
+  float* Ds = reinterpret_cast<float*>(lds + (long)oD * 16);
+
+  // ---- 2. gates: gamma_i = prod_{i<j<=w} g_j (lane i), Gamma = prod_{j<=w} g_j
+  const float gam = L <= 16 ? row16_suffix_product_exclusive(gl)
+                            : wave_suffix_product_exclusive(gl, lane);
+  const float Gam = lane_value(gl * gam, 0);
+
+  // ---- 3. ring dots kk_i = k_i . k_w, kq_i = k_i . q: 16 lanes per row i
+  float kk = 0.f, kq = 0.f;
   {
-    constexpr int DG = 16;
-    const int grp = tid / DG;
-    const int lane = tid % DG;
-    // 2w+1 dots: kk_i = k_i.k_w (i < w), kq_i = k_i.q (i <= w)
-    const int ndot = 2 * w + 1;
-    for (int t0 = 0; t0 < ndot; t0 += NT / DG) {
-      const int t = t0 + grp;
-      float acc = 0.f;
-      const bool live = t < ndot;
-      const int i = t <= w ? t : t - (w + 1);
-      const float* other = t <= w ? qs : ks + w * K;
-      if (live)
-        for (int n = lane; n < K; n += DG) acc = fmaf(ks[i * K + n], other[n], acc);
-      acc = group_sum<DG>(acc);
-      if (live && lane == 0) {
-        if (t <= w) kq[i] = acc;
-        else kk[i] = acc;
+    constexpr int EPL = K / 16;
+    const int q16 = lane & 15;
+    SegDot<IT, EPL> kw, qq;
+    kw.load(Ks + (long)w * QV * 16, q16 * EPL);
+    qq.load(Qs, q16 * EPL);
+    for (int pass = 0; pass * 4 <= w; ++pass) {
+      const int i = pass * 4 + (lane >> 4);
+      SegDot<IT, EPL> ki;
+      ki.load(Ks + (long)i * QV * 16, q16 * EPL);  // rows past w: unused values
+      float a1 = group_sum<16>(ki.dot(kw));
+      float a2 = group_sum<16>(ki.dot(qq));
+      a1 = __shfl(a1, (lane & 3) * 16, 64);
+      a2 = __shfl(a2, (lane & 3) * 16, 64);
+      if ((lane >> 2) == pass) {
+        kk = a1;
+        kq = a2;
       }
     }
   }
-  __syncthreads();
+  const float kqw = lane_value(kq, w);        // k_w . q
+  float* cw = cf_lds + wave * 128;            // [gamma_i kk_i (i<w) | gamma_i kq_i (i<w)]
+  cw[lane] = lane < w ? gam * kk : 0.f;
+  cw[64 + lane] = lane < w ? gam * kq : 0.f;
+  __builtin_amdgcn_wave_barrier();
 
-  // ---- 4. S0 @ k_w and S0 @ q per state row
+  // ---- 4. S0 . k_w and S0 . q per state row
   const int c = tid % LPR;
   const int prow = tid / LPR;
-  float kv4[SV], qv4[SV];
-#pragma unroll
-  for (int j = 0; j < SV; ++j) {
-    kv4[j] = ks[w * K + c * SV + j];
-    qv4[j] = qs[c * SV + j];
-  }
-  float dk_acc[ITEMS], dq_acc[ITEMS];
+  float kseg[SV], qseg[SV];
+  LdsRead<IT>::template seg<SV>(Ks + (long)w * QV * 16, c * SV, kseg);
+  LdsRead<IT>::template seg<SV>(Qs, c * SV, qseg);
+  float pk[ITEMS], pq[ITEMS];
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
     float sf[SV];
@@ -244,64 +269,105 @@ __global__ void __launch_bounds__(NT) gdn_decode_kernel(const GdnArgs a) {
     float a1 = 0.f, a2 = 0.f;
 #pragma unroll
     for (int j = 0; j < SV; ++j) {
-      a1 = fmaf(sf[j], kv4[j], a1);
-      a2 = fmaf(sf[j], qv4[j], a2);
+      a1 = fmaf(sf[j], kseg[j], a1);
+      a2 = fmaf(sf[j], qseg[j], a2);
     }
-    dk_acc[it] = group_sum<LPR>(a1);
-    dq_acc[it] = group_sum<LPR>(a2);
+    pk[it] = a1;
+    pq[it] = a2;
   }
-  const float Gam = scal[0];
-  const float bw = a.beta[(long)b * HV + hv];
-  // ---- 5. delta d_w and output (lane 0 of each row)
-  if (c == 0) {
+  using RR = RowReduce<ITEMS, LPR>;
+  RR::run(pk, tid);
+  RR::run(pq, tid);
+
+  // ---- 5. per state row: pred, d_w, o
+  const bool writer = (c % RR::DUP) == 0;
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int p = it * RPI + prow;
-      float pred = Gam * dk_acc[it];
-      float outv = Gam * dq_acc[it];
-      for (int i = 0; i < w; ++i) {
-        const float gd = gam[i] * ds[i * V + p];
-        pred = fmaf(gd, kk[i], pred);
-        outv = fmaf(gd, kq[i], outv);
+  for (int j = 0; j < RR::NF; ++j) {
+    const int vr = RR::item(j, tid) * RPI + prow;
+    float pred = Gam * pk[j];
+    float outv = Gam * pq[j];
+    for (int ib = 0; ib < w; ib += 4) {
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        const int i = ib + k2;
+        const int ic = i < w ? i : w - 1;  // weights are 0 past w-1
+        const float dv = Ds[ic * V + vr];
+        pred = fmaf(cw[i], dv, pred);
+        outv = fmaf(cw[64 + i], dv, outv);
       }
-      const float dw = bw * (vs[p] - pred);
-      outv = fmaf(dw, kq[w], outv);
-      ds[w * V + p] = dw;
-      Elt<OT>::store1(a.o, ooff + p, a.scale * outv);
-      if (append) a.d_ring[dring0 + (long)w * V + p] = dw;
+    }
+    const float dw = bw * (LdsRead<IT>::one(Vs, vr) - pred);
+    outv = fmaf(kqw, dw, outv);
+    if (writer) {
+      Elt<OT>::store1(a.o, ooff + vr, a.scale * outv);
+      Ds[w * V + vr] = dw;
     }
   }
-  if (f) {
-    __syncthreads();
-    // ---- 6. fold: S_new = Gamma * S0 + sum_i gamma_i * outer(d_i, k_i)
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const int p = it * RPI + prow;
-      float sf[SV];
-      Elt<float>::unpack(sv[it], sf);
-#pragma unroll
-      for (int j = 0; j < SV; ++j) sf[j] *= Gam;
-      for (int i = 0; i <= w; ++i) {
-        const float coef = gam[i] * ds[i * V + p];
-        const float* kp = ks + i * K + c * SV;
-#pragma unroll
-        for (int j = 0; j < SV; ++j) sf[j] = fmaf(coef, kp[j], sf[j]);
+  if (wave == 0) gm_lds[lane] = gam;
+  __syncthreads();  // d_w of every row and the gamma_i are in LDS
+
+  if (!f) {
+    // ---- 6a. append (d_w, k_w, g_w) at ring position w
+    if (wave == 0) {
+      const bool k_writer = (hv % a.vpk) == 0;  // one writer per key head
+      for (int k2 = lane; k2 < DV + QV; k2 += 64) {
+        if (k2 < DV) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(lds + ((long)oD + w * DV + k2) * 16);
+          st16(a.d_ring, (dring0 + (long)w * V) * 4 + k2 * 16, v);
+        } else if (k_writer) {
+          const int cc = k2 - DV;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(Ks + ((long)w * QV + cc) * 16);
+          st16(a.k_ring, (kring0 + (long)w * K) * kIo + cc * 16, v);
+        }
       }
-      st16_stream(a.state, tile_byte + ((long)it * NT + tid) * 16, Elt<float>::pack(sf));
+      if (lane == 0) a.g_ring[gring0 + w] = gw;
+    }
+    return;
+  }
+
+  // ---- 6b. flush: S_new = Gamma*S0 + sum_{i<=w} outer(gamma_i d_i, k_i)
+  for (int e = tid; e < (w + 1) * V; e += NT) {
+    const int i = e / V;
+    Ds[e] *= gm_lds[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i0 = 0; i0 < ITEMS; i0 += IC) {
+    float sf[IC][SV];
+#pragma unroll
+    for (int q = 0; q < IC; ++q)
+#pragma unroll
+      for (int j = 0; j < SV; ++j) sf[q][j] = 0.f;
+    for (int i = 0; i <= w; ++i) {
+      float kv[SV];
+      LdsRead<IT>::template seg<SV>(Ks + (long)i * QV * 16, c * SV, kv);
+#pragma unroll
+      for (int q = 0; q < IC; ++q) {
+        const float dv = Ds[i * V + (i0 + q) * RPI + prow];
+#pragma unroll
+        for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(dv, kv[j], sf[q][j]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < IC; ++q) {
+      float s0[SV];
+      Elt<float>::unpack(sv[i0 + q], s0);
+#pragma unroll
+      for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(Gam, s0[j], sf[q][j]);
+      st16_stream(tptr, (long)lane_off + (i0 + q) * NT * 16, Elt<float>::pack(sf[q]));
     }
   }
 }
 
 template <typename IT, typename OT, int V, int K, bool REPLAY>
 static int launch_gdn(const GdnArgs& a, int batch, hipStream_t stream) {
-  constexpr int NVEC = V * K / 4;
-  constexpr int NT = NVEC >= 512 ? 512 : NVEC;
-  const int L = REPLAY ? a.ring_len : 1;
-  const size_t lds = sizeof(float) * (size_t)gdn_lds_floats<V, K>(L);
-  if (lds > kMaxLds) return RSSM_ESHAPE;  // ring rows must fit one workgroup's LDS
-  return launch_kernel(
-      reinterpret_cast<const void*>(&gdn_decode_kernel<IT, OT, V, K, NT, REPLAY>),
-      (unsigned)((long)batch * a.v_heads), NT, lds, stream, a);
+  using GS = GdnShape<V, K, REPLAY>;
+  const int L = REPLAY ? a.ring_len : 1;  // L <= 64: one gate per lane of a wave
+  const size_t lds = (size_t)GdnStage<IT, V, K>::chunks(L) * 16;
+  const size_t fixed = (2 * GS::NT + 64) * sizeof(float);  // weight and gate arrays
+  if (lds + fixed > kMaxLds) return RSSM_ESHAPE;  // ring rows must fit one workgroup's LDS
+  return launch_kernel(reinterpret_cast<const void*>(&gdn_decode_kernel<IT, OT, V, K, REPLAY>),
+                       (unsigned)((long)batch * a.v_heads), GS::NT, lds, stream, a);
 }
 
 template <bool REPLAY, typename IT, typename OT>

@@ -243,6 +243,7 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
   constexpr long kIo = sizeof(IT);
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ __attribute__((aligned(16))) float coef_lds[NT];  // ring-term weights per wave
 
   const int L = REPLAY ? a.ring_len : 1;
   const int H = a.nheads;
@@ -302,38 +303,56 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
   const int nAll = oB + (w + 1) * BV;
 
   // Stage C, z, x_0..x_w, B_0..B_w (entry w = the current step) into LDS
-  // with direct-to-LDS loads, and load dt of entries 0..w (lane i).
-  auto stage = [&]() {
-    for (int k = 0; k * NT < nAll; ++k) {
-      const int u = k * NT + tid;
-      if (u < nAll) {
-        const char* src;
-        if (u < BV) {
-          src = (const char*)a.C + (bccur * kIo + (long)u * 16);
-        } else if (u < oX) {
-          src = (const char*)a.z + (xcur * kIo + (long)(u - BV) * 16);
-        } else if (u < oB) {
-          const int i = (u - oX) / XV, cc = (u - oX) - i * XV;
-          src = (REPLAY && i < w)
-                    ? (const char*)a.x_ring + ((xring0 + (long)i * P) * kIo + cc * 16)
-                    : (const char*)a.x + (xcur * kIo + cc * 16);
-        } else {
-          const int i = (u - oB) / BV, cc = (u - oB) - i * BV;
-          src = (REPLAY && i < w)
-                    ? (const char*)a.B_ring + ((bring0 + (long)i * N) * kIo + cc * 16)
-                    : (const char*)a.B + (bccur * kIo + cc * 16);
-        }
-        dma16(src, lds + ((long)k * NT + wave * 64) * 16);
+  // with direct-to-LDS loads, one contiguous global span at a time (the w
+  // ring rows of a slot are contiguous), and load dt of entries 0..w (lane i).
+  // span: LDS chunks [c0, c0+n); the first nring from `ring`, then `cur`.
+  auto dma_span = [&](int c0, int n, const char* ring, int nring, const char* cur) {
+    for (int j = wave * 64; j < n; j += NT) {
+      const int u = j + lane;
+      if (u < n) {
+        const char* src = u < nring ? ring + (long)u * 16 : cur + (long)(u - nring) * 16;
+        dma16(src, lds + (long)(c0 + j) * 16);
       }
     }
   };
-  float dti = 0.f;
-  if (REPLAY && lane < w) dti = a.dt_ring[dtring0 + lane];
-  {
-    const float v = Elt<IT>::load1(a.dt, (long)b * H + h) + (a.dt_bias ? a.dt_bias[h] : 0.f);
+  auto stage = [&]() {
+    if constexpr (!REPLAY) {
+      // no ring: C, z, x, B are at most a few dozen chunks, one per lane
+      for (int u = tid; u < nAll; u += NT) {
+        const char* src;
+        if (u < BV) src = (const char*)a.C + (bccur * kIo + (long)u * 16);
+        else if (u < oX) src = (const char*)a.z + (xcur * kIo + (long)(u - BV) * 16);
+        else if (u < oB) src = (const char*)a.x + (xcur * kIo + (long)(u - oX) * 16);
+        else src = (const char*)a.B + (bccur * kIo + (long)(u - oB) * 16);
+        dma16(src, lds + (long)(u - lane) * 16);
+      }
+      return;
+    }
+    const char* cg = (const char*)a.C + bccur * kIo;
+    dma_span(0, BV, cg, BV, cg);
+    if (a.z) {
+      const char* zg = (const char*)a.z + xcur * kIo;
+      dma_span(BV, XV, zg, XV, zg);
+    }
+    dma_span(oX, (w + 1) * XV, REPLAY ? (const char*)a.x_ring + xring0 * kIo : nullptr,
+             REPLAY ? w * XV : 0, (const char*)a.x + xcur * kIo);
+    dma_span(oB, (w + 1) * BV, REPLAY ? (const char*)a.B_ring + bring0 * kIo : nullptr,
+             REPLAY ? w * BV : 0, (const char*)a.B + bccur * kIo);
+  };
+  // dt of entries 0..w (lane i): the loads are issued after the tile reads
+  // (load_dt), the bias and softplus applied after the wait (finish_dt), so
+  // no scalar round trip sits in front of the tile stream.
+  float dti = 0.f, dtr = 0.f, dtb = 0.f;
+  auto load_dt = [&]() {
+    if (REPLAY && lane < w) dti = a.dt_ring[dtring0 + lane];
+    dtr = Elt<IT>::load1(a.dt, (long)b * H + h);
+    if (a.dt_bias) dtb = a.dt_bias[h];
+  };
+  auto finish_dt = [&]() {
+    const float v = dtr + dtb;
     const float dcur = a.dt_softplus ? softplus_f32(v) : v;
     if (lane == w) dti = dcur;
-  }
+  };
   const float Ah = a.A[h];
   const float Dh = a.D ? a.D[h] : 0.f;
 
@@ -352,8 +371,10 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
     stage();
+    load_dt();
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    finish_dt();
     // append the current step at ring position w (replay only: the standard
     // update has no ring and never reaches this branch)
     if (REPLAY && wave == 0) {
@@ -394,6 +415,8 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
         if ((lane >> 3) == q) bc = t;
       }
       coef = lane <= w ? wt * bc : 0.f;
+      coef_lds[wave * 64 + lane] = coef;  // broadcast to the wave through LDS
+      __builtin_amdgcn_wave_barrier();
     }
     // S0 . C per state row
     RowDot<ST, IT, SV> rd;
@@ -410,8 +433,10 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
       for (int q = 0; q < IC; ++q) rb[q] = bload16_nt(trs, lane_off, (IC + q) * NT * 16);
     }
     stage();
+    load_dt();
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    finish_dt();
     const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
     cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
     const float wt = lane <= w ? dti * expf(Ah * rsuf) : 0.f;
@@ -434,11 +459,11 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
     if (!f) {
       // coef is 0 past w; row indexes are clamped to w
       yv *= cumdecay;
+      const float* cw = coef_lds + wave * 64;
 #pragma unroll
       for (int i = 0; i < 16; ++i)
-        yv = fmaf(lane_value(coef, i), LdsRead<IT>::one(xs, (i <= w ? i : w) * P + p), yv);
-      for (int i = 16; i <= w; ++i)
-        yv = fmaf(lane_value(coef, i), LdsRead<IT>::one(xs, i * P + p), yv);
+        yv = fmaf(cw[i], LdsRead<IT>::one(xs, (i <= w ? i : w) * P + p), yv);
+      for (int i = 16; i <= w; ++i) yv = fmaf(cw[i], LdsRead<IT>::one(xs, i * P + p), yv);
     }
     yv = fmaf(Dh, LdsRead<IT>::one(xs, w * P + p), yv);
     if (a.z) yv = silu_gate(yv, LdsRead<IT>::one(zs, p));

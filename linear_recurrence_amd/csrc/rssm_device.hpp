@@ -162,6 +162,25 @@ __device__ static inline float row16_suffix_exclusive(float v) {
   return r;
 }
 
+// Row shift within rows of 16 lanes (DPP) where lanes past the end of the
+// row keep `fill`.
+template <int K>
+__device__ static inline float row_shl_fill(float v, float fill) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v),
+                                                    0x100 + K, 0xF, 0xF, false));
+}
+
+// Exclusive suffix product over lanes 0..15: lane i < 16 receives
+// prod_{i<j<16} v_j (1 for lane 15).
+__device__ static inline float row16_suffix_product_exclusive(float v) {
+  float r = row_shl_fill<1>(v, 1.f);
+  r *= row_shl_fill<1>(r, 1.f);
+  r *= row_shl_fill<2>(r, 1.f);
+  r *= row_shl_fill<4>(r, 1.f);
+  r *= row_shl_fill<8>(r, 1.f);
+  return r;
+}
+
 // Exclusive suffix product across the wave: lane i receives prod_{j>i} v_j.
 __device__ static inline float wave_suffix_product_exclusive(float v, int lane) {
   float r = __shfl_down(v, 1, 64);
@@ -267,12 +286,20 @@ template <> struct LdsRead<bf16> {
   }
 };
 
+// softplus(v) = log(1 + e^v): v itself above 20 (exact in fp32).  log1p(e)
+// is taken as log(u) * e / (u - 1) with u = 1 + e, which cancels the
+// rounding of u (u - 1 is exact; accurate to a few ulp with the hardware log
+// and reciprocal), and is e itself when u rounds to 1.
 __device__ static inline float softplus_f32(float v) {
-  return v > 20.f ? v : log1pf(expf(v));
+  if (v > 20.f) return v;
+  const float e = expf(v);
+  const float u = 1.f + e;
+  return u == 1.f ? e : __logf(u) * (e * __builtin_amdgcn_rcpf(u - 1.f));
 }
 
+// y * z * sigmoid(z) with the hardware exp and reciprocal (about 2 ulp).
 __device__ static inline float silu_gate(float y, float z) {
-  return y * (z / (1.f + expf(-z)));
+  return y * (z * __builtin_amdgcn_rcpf(1.f + __expf(-z)));
 }
 
 }  // namespace rssm

@@ -41,3 +41,12 @@ def test_gdn_full_size_desynced_rows():
     wl = GdnWorkload("gdn_b256_desync", 256, 16, 32, 128, 128, 16, 40, 512, "bf16", "f32",
                      1004, desync=True)
     run_gdn(wl, sample=[3, 77, 150, 222], standard=False)
+
+
+@pytest.mark.parametrize("L", [5, 17, 32, 64])
+def test_gdn_long_rings(L):
+    """Rings past one 16-lane row of gates (suffix products over the wave),
+    up to the 64-entry maximum; bf16 q/k/v keep the staged rows within LDS."""
+    wl = GdnWorkload(f"gdn_L{L}", 3, 2, 4, 128, 128, L, 2 * L + 3, 6, "bf16", "f32",
+                     3200 + L, desync=True)
+    run_gdn(wl, sample=range(3), check_every=max(1, L // 8))
