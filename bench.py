@@ -20,8 +20,9 @@ Roofline: algorithmic bytes per launch (checkpoint reads, ring reads of the
 live entries, ring appends, flush write-backs, step inputs, outputs and
 metadata, evaluated exactly from every row's cursor at that step) divided by
 the average launch time measured with HIP events on the launch stream.
-``traffic`` comes from rocprofv3 FETCH_SIZE / WRITE_SIZE counters when given
-with --traffic-json (see profiles/).
+``traffic`` is the HBM bytes per replay launch from rocprofv3 FETCH_SIZE /
+WRITE_SIZE counters (profiles/replayssm_decode_mamba2_b512_traffic.json),
+reported only while its source fingerprint matches the kernel sources.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 4]
        python bench.py --copy-probe      (copy kernel for counter calibration)
@@ -41,6 +42,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "replayssm_decode_mamba2_b512_traffic.json")
 METRIC = "decode state-updates/s + achieved HBM GB/s (% peak), Mamba2 B=512 L=16"
 
 
@@ -295,6 +297,21 @@ def cpu_baseline(wl, rows, steps):
                       f"steps ({L} desync warm-up steps first), one thread, {dt:.1f} s"}
 
 
+def measured_traffic(path):
+    """HBM bytes per replay launch from the committed counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    from linear_recurrence_amd.profsum import source_sha256
+    if not path or not os.path.exists(path):
+        return None, "no counter summary"
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_sha256") != source_sha256("mamba2_decode_kernel"):
+        return None, f"{os.path.relpath(path, ROOT)} predates the current kernel sources"
+    return t["bytes_per_launch"], (
+        f"{os.path.relpath(path, ROOT)}: FETCH_SIZE x {t['fetch_factor']:.3f} + "
+        f"WRITE_SIZE x {t['write_factor']:.3f} per replay dispatch (copy-kernel scaled)")
+
+
 def copy_probe(dev, gib=1.0, reps=5):
     """A plain device copy of known size, for scaling HBM counters."""
     n = int(gib * (1 << 30)) // 4
@@ -320,9 +337,9 @@ def main():
     ap.add_argument("--y-dtype", choices=("bf16", "f32"), default="bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-gdn", action="store_true", help="skip the GDN measurement")
-    ap.add_argument("--cpu-rows", type=int, default=48)
-    ap.add_argument("--cpu-steps", type=int, default=32)
-    ap.add_argument("--traffic-json", default=None,
+    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--cpu-steps", type=int, default=80)
+    ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
                     help="per-launch HBM bytes measured with rocprofv3 counters")
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
@@ -362,10 +379,7 @@ def main():
 
     ms_per_step = m["replay_s"] / args.steps * 1e3
     achieved = m["replay_bytes_per_launch"] / (m["replay_s"] / args.steps) / 1e9
-    traffic = None
-    if args.traffic_json:
-        with open(args.traffic_json) as fh:
-            traffic = json.load(fh).get("replayssm_decode_bytes_per_launch")
+    traffic, traffic_note = measured_traffic(args.traffic_json)
     line = {
         "metric": METRIC,
         "value": m["replay_updates_per_s"],
@@ -392,6 +406,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+            "traffic_source": traffic_note,
             "kernel": "replayssm_decode (mamba2_decode_kernel, replay)",
             "algorithmic_bytes_per_launch": m["replay_bytes_per_launch"],
         },

@@ -1,0 +1,138 @@
+"""Summaries of rocprofv3 output for the decode kernels.
+
+    python -m linear_recurrence_amd.profsum stats RUN_kernel_stats.csv --command "..."
+        Markdown table of per-kernel launch counts and durations.
+
+    python -m linear_recurrence_amd.profsum traffic --fetch BENCH_FETCH.csv \
+        --write BENCH_WRITE.csv --copy-fetch COPY_FETCH.csv --copy-write COPY_WRITE.csv \
+        --kernel mamba2_decode_kernel --replay --last 32 --copy-bytes 1073741824
+        HBM bytes per launch of one kernel from the FETCH_SIZE and WRITE_SIZE
+        counters (KiB per dispatch), each scaled by the ratio between the known
+        size of a plain device copy and what the same counter reads for it.
+        Prints JSON; ``source_sha256`` fingerprints the kernel sources the
+        counters were taken on, so a reader can tell when they are stale.
+"""
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+KERNEL_SOURCES = {
+    "mamba2_decode_kernel": ("mamba2_decode.hip", "rssm_device.hpp", "rssm_host.hpp"),
+    "gdn_decode_kernel": ("gdn_decode.hip", "rssm_device.hpp", "rssm_host.hpp"),
+}
+
+
+def source_sha256(kernel):
+    """SHA-256 over the source files a kernel is compiled from."""
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, name), "rb") as fh:
+            h.update(name.encode())
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _rows(path):
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _is_replay(name):
+    # template argument REPLAY is the last one: "..., true>(" / "..., false>("
+    return name.rstrip().endswith("true>(rssm::Mamba2Args)") or \
+        name.rstrip().endswith("true>(rssm::GdnArgs)")
+
+
+def _dispatch_kib(path, kernel, replay, last):
+    """Counter value (KiB) per dispatch of `kernel`, the last `last` ones."""
+    per = {}
+    for r in _rows(path):
+        name = r["Kernel_Name"]
+        if kernel not in name or _is_replay(name) != replay:
+            continue
+        d = int(r["Dispatch_Id"])
+        per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)[-last:] if last else sorted(per)
+    if not ids:
+        raise SystemExit(f"no dispatches of {kernel} (replay={replay}) in {path}")
+    return [per[i] for i in ids]
+
+
+def _copy_factor(path, known_bytes):
+    """known bytes / counter bytes for the largest dispatches (the probe copies)."""
+    per = {}
+    for r in _rows(path):
+        d = int(r["Dispatch_Id"])
+        per[d] = per.get(d, 0.0) + float(r["Counter_Value"])
+    vals = sorted(per.values())
+    big = [v for v in vals if v >= 0.5 * vals[-1]]
+    kib = sum(big) / len(big)
+    return known_bytes / (kib * 1024.0), kib
+
+
+def cmd_stats(args):
+    rows = _rows(args.csv)
+    out = []
+    if args.command:
+        out.append("Command:\n\n```\n" + args.command + "\n```\n")
+    out.append("| kernel | calls | avg us | min us | max us | share |")
+    out.append("|---|---:|---:|---:|---:|---:|")
+    for r in rows:
+        name = r["Name"] if "rssm::" in r["Name"] else r["Name"][:60] + "..."
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    print("\n".join(out))
+
+
+def cmd_traffic(args):
+    ff, fkib = _copy_factor(args.copy_fetch, args.copy_bytes)
+    wf, wkib = _copy_factor(args.copy_write, args.copy_bytes)
+    fetch = _dispatch_kib(args.fetch, args.kernel, args.replay, args.last)
+    write = _dispatch_kib(args.write, args.kernel, args.replay, args.last)
+    fb = sum(fetch) / len(fetch) * 1024.0 * ff
+    wb = sum(write) / len(write) * 1024.0 * wf
+    res = {
+        "kernel": args.kernel + (" (replay)" if args.replay else " (standard)"),
+        "dispatches": [len(fetch), len(write)],
+        "fetch_kib_per_dispatch": sum(fetch) / len(fetch),
+        "write_kib_per_dispatch": sum(write) / len(write),
+        "copy_probe_bytes": args.copy_bytes,
+        "copy_fetch_kib": fkib, "copy_write_kib": wkib,
+        "fetch_factor": ff, "write_factor": wf,
+        "fetch_bytes_per_launch": fb, "write_bytes_per_launch": wb,
+        "bytes_per_launch": fb + wb,
+        "source_sha256": source_sha256(args.kernel),
+    }
+    if args.command:
+        res["commands"] = args.command
+    print(json.dumps(res, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    s.add_argument("--command", default=None)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
+    t.add_argument("--replay", action="store_true")
+    t.add_argument("--last", type=int, default=0)
+    t.add_argument("--copy-bytes", type=float, default=float(1 << 30))
+    t.add_argument("--command", action="append", default=None)
+    args = ap.parse_args(argv)
+    {"stats": cmd_stats, "traffic": cmd_traffic}[args.mode](args)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
