@@ -21,7 +21,8 @@
  *    item 1 (ring cursors are reset when a slot is reused).
  *
  * Conventions shared by every entry point
- *  - Every pointer is a DEVICE pointer to memory the caller owns, allocated
+ *  - Every pointer is a DEVICE pointer to memory the caller owns (except
+ *    for the host-side metadata helpers at the end), allocated
  *    on the device that is current when the call is made.  The library never
  *    allocates, frees or synchronises, keeps no global mutable state, and is
  *    re-entrant: it validates the arguments, enqueues kernels on `stream`
@@ -220,6 +221,45 @@ int replayssm_gdn_decode(const rssm_gdn_dims* dims, void* state, float* d_ring,
                          const void* q, const void* k, const void* v,
                          const float* g, const float* beta, void* o,
                          int32_t* status, hipStream_t stream);
+
+/*
+ * Host-side metadata (HOST pointers; plain CPU code, nothing is enqueued).
+ *
+ * replayssm_build_metadata - per-row cursors of one decode step from token
+ * positions (vLLM #48018, Implementation item 3: write_pos and is_flush come
+ * from a per-request decode base; align-mode re-anchoring; review notes on
+ * the flush boundary, one-token prefills and preemption).  For row r:
+ *     pos[r]          index of the token decoded in this step (tokens before it)
+ *     decode_base[r]  number of tokens folded into the row's checkpoint S0;
+ *                     set it to the prefill length for a fresh request, and
+ *                     to the re-prefilled length when a preempted request
+ *                     resumes (re-anchoring)
+ *     w = pos - decode_base, which must lie in [0, ring_len)
+ *     f = (w == ring_len-1) || force_flush[r] ||
+ *         (align_block > 0 && (pos+1) % align_block == 0)
+ * Writes write_pos[r] = w, is_flush[r] = f, and decode_base[r] = pos+1 when
+ * f (the checkpoint will hold this token once the step has run).  With
+ * align_block > 0 every checkpoint lands on a multiple of align_block or on
+ * a ring-full boundary, so a prefix cache can snapshot block-aligned states.
+ * force_flush may be NULL.  Returns RSSM_EINVAL, writing nothing, if any row
+ * is out of range (w < 0, w >= ring_len, negative positions) or on bad
+ * arguments.  For rows advancing one token per step this reproduces the
+ * device-side cursor advance of replayssm_decode.
+ */
+int replayssm_build_metadata(int32_t n_rows, int32_t ring_len, int32_t align_block,
+                             const int64_t* pos, int64_t* decode_base,
+                             const uint8_t* force_flush, int32_t* write_pos,
+                             uint8_t* is_flush);
+
+/*
+ * replayssm_check_copy_sources - the copy rule for slots (sglang #28451 and
+ * #28695: a slot's state may be copied only when its ring is empty, else
+ * the ring entries not yet folded would be lost).  src_write_pos [n] are the
+ * current write positions of the source rows (HOST pointer).  RSSM_OK if
+ * every one is 0, RSSM_EINVAL otherwise.  After copying a state into a new
+ * slot, reset that row's cursors with replayssm_ring_reset.
+ */
+int replayssm_check_copy_sources(int32_t n, const int32_t* src_write_pos);
 
 /* Human-readable text of a return code (static storage). */
 const char* replayssm_strerror(int code);

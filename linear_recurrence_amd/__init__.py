@@ -19,7 +19,8 @@ import torch  # loads the HIP runtime the library then binds to
 
 __all__ = [
     "ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
-    "gdn_standard_decode", "replayssm_gdn_decode", "library_path", "load",
+    "gdn_standard_decode", "replayssm_gdn_decode", "build_metadata",
+    "check_copy_sources", "library_path", "load",
     "RssmError", "ST_BAD_WRITE_POS", "ST_RING_OVERFLOW", "ST_BAD_SLOT",
     "ST_BAD_ROW", "EXPORTS",
 ]
@@ -29,8 +30,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libreplayss
 F32, BF16 = 0, 1
 ST_BAD_WRITE_POS, ST_RING_OVERFLOW, ST_BAD_SLOT, ST_BAD_ROW = 1, 2, 4, 8
 EXPORTS = ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
-           "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_strerror",
-           "replayssm_abi_version")
+           "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_build_metadata",
+           "replayssm_check_copy_sources", "replayssm_strerror", "replayssm_abi_version")
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
@@ -80,6 +81,10 @@ def load():
     for fn in ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
                "gdn_standard_decode", "replayssm_gdn_decode"):
         getattr(lib, fn).restype = ctypes.c_int
+    lib.replayssm_build_metadata.argtypes = [I, I, I, P, P, P, P, P]
+    lib.replayssm_build_metadata.restype = ctypes.c_int
+    lib.replayssm_check_copy_sources.argtypes = [I, P]
+    lib.replayssm_check_copy_sources.restype = ctypes.c_int
     lib.replayssm_strerror.argtypes = [ctypes.c_int]
     lib.replayssm_strerror.restype = ctypes.c_char_p
     lib.replayssm_abi_version.restype = ctypes.c_int
@@ -227,6 +232,47 @@ def replayssm_ring_reset(write_pos, is_flush, rows, ring_len, status=None,
         ctypes.byref(d), _ptr(write_pos), _ptr(is_flush), _ptr(rows),
         ctypes.c_int32(rows.numel()), _ptr(status), _stream(stream))
     _check("replayssm_ring_reset", rc)
+
+
+def _host(a, name, dtype, n=None):
+    import numpy as np
+    if not isinstance(a, np.ndarray) or a.dtype != dtype or a.ndim != 1 or \
+            not a.flags.c_contiguous:
+        raise TypeError(f"{name} must be a contiguous 1-D numpy {np.dtype(dtype)} array")
+    if n is not None and a.shape[0] != n:
+        raise ValueError(f"{name} must have {n} entries")
+    return ctypes.c_void_p(a.ctypes.data) if a.size else None
+
+
+def build_metadata(pos, decode_base, ring_len, force_flush=None, align_block=0):
+    """Host-side cursors of one decode step (numpy arrays, see the header).
+
+    pos, decode_base: int64 [n] (decode_base is updated in place on flush
+    rows); force_flush: optional uint8 [n].  Returns (write_pos int32 [n],
+    is_flush uint8 [n]) as numpy arrays.
+    """
+    import numpy as np
+    n = pos.shape[0] if hasattr(pos, "shape") else 0
+    pp = _host(pos, "pos", np.int64)
+    bp = _host(decode_base, "decode_base", np.int64, n)
+    fp = None if force_flush is None else _host(force_flush, "force_flush", np.uint8, n)
+    wp = np.zeros(n, np.int32)
+    fl = np.zeros(n, np.uint8)
+    rc = load().replayssm_build_metadata(
+        ctypes.c_int32(n), ctypes.c_int32(ring_len), ctypes.c_int32(align_block), pp, bp, fp,
+        ctypes.c_void_p(wp.ctypes.data) if n else None,
+        ctypes.c_void_p(fl.ctypes.data) if n else None)
+    _check("replayssm_build_metadata", rc)
+    return wp, fl
+
+
+def check_copy_sources(src_write_pos):
+    """Raise unless every source row's ring is empty (write position 0)."""
+    import numpy as np
+    n = src_write_pos.shape[0]
+    rc = load().replayssm_check_copy_sources(
+        ctypes.c_int32(n), _host(src_write_pos, "src_write_pos", np.int32))
+    _check("replayssm_check_copy_sources", rc)
 
 
 def _gdn_dims(state, q, v, ring_len, o_dtype, scale):

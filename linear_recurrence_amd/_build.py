@@ -1,7 +1,8 @@
 """Build libreplayssm.so in-tree with hipcc for gfx950.
 
 Usage: python -m linear_recurrence_amd._build   (or __graft_entry__.build()).
-Each HIP source compiles to an object in parallel; the objects link into
+Each HIP source compiles to an object in parallel (the host-only metadata
+helpers with the host C++ compiler); the objects link into
 ``linear_recurrence_amd/libreplayssm.so``.
 """
 
@@ -15,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libreplayssm.so")
-SOURCES = ("mamba2_decode.hip", "gdn_decode.hip")
+SOURCES = ("mamba2_decode.hip", "gdn_decode.hip", "metadata.cpp")
+CXX = os.environ.get("CXX", "g++")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -29,11 +31,17 @@ FLAGS = [
 
 
 def _compile(src):
-    out = os.path.join(OBJ, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+    out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
+    if src.endswith(".cpp"):  # host-only code
+        inc = ["-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include",
+               "-D__HIP_PLATFORM_AMD__"]
+        cmd = [CXX, "-O2", "-std=c++17", "-fPIC", "-Wall", *inc, "-c",
+               os.path.join(CSRC, src), "-o", out]
+    else:
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
-        raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        raise RuntimeError(f"compile failed for {src}:\n{r.stderr}")
     return out
 
 

@@ -27,6 +27,7 @@ Modules
 ``mamba2``    standard selective state update (the recurrence) and the
               ReplaySSM ring replay with flush, cursor advance and ring reset.
 ``gdn``       gated delta rule: recurrence and ring replay.
+``metadata``  host cursors of a step from token positions (decode base).
 """
 
-from . import numerics, mamba2, gdn  # noqa: F401
+from . import numerics, mamba2, gdn, metadata  # noqa: F401
