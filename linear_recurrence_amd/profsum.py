@@ -3,6 +3,12 @@
     python -m linear_recurrence_amd.profsum stats RUN_kernel_stats.csv --command "..."
         Markdown table of per-kernel launch counts and durations.
 
+    python -m linear_recurrence_amd.profsum sq RUN_counter_collection.csv --last 32
+        Per-kernel SQ instruction counts per wave and the VALU issue share:
+        SQ_INSTS_VALU * 4 cycles (a wave64 VALU instruction on a 16-lane SIMD)
+        / (1024 SIMDs * GRBM_GUI_ACTIVE / 8), GRBM_GUI_ACTIVE being summed over
+        the 8 XCDs.
+
     python -m linear_recurrence_amd.profsum traffic --fetch BENCH_FETCH.csv \
         --write BENCH_WRITE.csv --copy-fetch COPY_FETCH.csv --copy-write COPY_WRITE.csv \
         --kernel mamba2_decode_kernel --replay --last 32 --copy-bytes 1073741824
@@ -90,6 +96,36 @@ def cmd_stats(args):
     print("\n".join(out))
 
 
+def cmd_sq(args):
+    per, name = {}, {}
+    for r in _rows(args.csv):
+        d = int(r["Dispatch_Id"])
+        c = per.setdefault(d, {})
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        name[d] = r["Kernel_Name"]
+    groups = {}
+    for d in sorted(per):
+        if "rssm::" in name[d]:
+            groups.setdefault(name[d], []).append(per[d])
+    out = []
+    if args.command:
+        out.append("Command:\n\n```\n" + args.command + "\n```\n")
+    out.append("| kernel | dispatches | waves | VALU/wave | SALU/wave | LDS/wave | "
+               "active us | VALU issue share | wait share of wave cycles |")
+    out.append("|---|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for n, lst in groups.items():
+        lst = lst[-args.last:] if args.last else lst
+        avg = {k: sum(c[k] for c in lst) / len(lst) for k in lst[0]}
+        w = avg["SQ_WAVES"]
+        gui = avg["GRBM_GUI_ACTIVE"] / 8.0
+        share = avg["SQ_INSTS_VALU"] * 4.0 / (1024.0 * gui)
+        out.append(f"| `{n}` | {len(lst)} | {w:.0f} | {avg['SQ_INSTS_VALU'] / w:.0f} | "
+                   f"{avg['SQ_INSTS_SALU'] / w:.0f} | {avg['SQ_INSTS_LDS'] / w:.0f} | "
+                   f"{gui / 2400.0:.1f} | {share:.2f} | "
+                   f"{avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.2f} |")
+    print("\n".join(out))
+
+
 def cmd_traffic(args):
     ff, fkib = _copy_factor(args.copy_fetch, args.copy_bytes)
     wf, wkib = _copy_factor(args.copy_write, args.copy_bytes)
@@ -120,6 +156,10 @@ def main(argv=None):
     s = sub.add_parser("stats")
     s.add_argument("csv")
     s.add_argument("--command", default=None)
+    q = sub.add_parser("sq")
+    q.add_argument("csv")
+    q.add_argument("--last", type=int, default=0)
+    q.add_argument("--command", default=None)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -131,7 +171,7 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=float, default=float(1 << 30))
     t.add_argument("--command", action="append", default=None)
     args = ap.parse_args(argv)
-    {"stats": cmd_stats, "traffic": cmd_traffic}[args.mode](args)
+    {"stats": cmd_stats, "sq": cmd_sq, "traffic": cmd_traffic}[args.mode](args)
 
 
 if __name__ == "__main__":
