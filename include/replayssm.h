@@ -75,6 +75,22 @@ enum {
 };
 
 /*
+ * Rounding of the bf16 state write-back (vLLM #48018, review notes:
+ * stochastic rounding was added for quantised models whose baseline relies
+ * on it).  RSSM_ROUND_STOCHASTIC rounds each element of a written bf16
+ * state tile up or down with probability given by the dropped 16 bits of its
+ * fp32 value, using 16 random bits per element from Philox4x64-10 (Salmon
+ * et al., SC 2011) with key (sr_seed, sr_offset) and counter
+ * (tile * P*N/16 + e/16, 0, 0, 0), tile = slot * nheads + head, e = p*N + n:
+ * element e takes bits 16*(e%4).. of output word (e%16)/4 and its bf16 bit
+ * pattern is (fp32 bits + those 16 bits) >> 16 (Inf and NaN round to
+ * nearest).  Applies to every state store of ssu_standard_decode and to the
+ * flush write-back of replayssm_decode.  Other values: RSSM_EINVAL;
+ * stochastic with an fp32 state: RSSM_EDTYPE.
+ */
+enum { RSSM_ROUND_NEAREST = 0, RSSM_ROUND_STOCHASTIC = 1 };
+
+/*
  * Mamba2 dimensions.  Supported: headdim in {32, 64, 128}; dstate in {16,
  * 32, 64, 128, 256}; 1 <= ring_len <= 64 with the ring rows a workgroup
  * stages, about 4*ring_len*(P+N) bytes, within 64 KB (RSSM_ESHAPE otherwise);
@@ -93,6 +109,11 @@ typedef struct rssm_dims {
   int32_t io_dtype;    /* x, z, dt, B, C and the x / B rings                */
   int32_t out_dtype;   /* y                                                 */
   int32_t dt_softplus; /* nonzero: dt = softplus(dt + dt_bias)              */
+  int32_t rounding;    /* state write-back: RSSM_ROUND_NEAREST or           */
+                       /* RSSM_ROUND_STOCHASTIC (bf16 state only)           */
+  uint64_t sr_seed;    /* stochastic rounding: Philox key word 0            */
+  uint64_t sr_offset;  /* stochastic rounding: Philox key word 1; change it */
+                       /* on every call so each write-back draws new bits   */
 } rssm_dims;
 
 /*

@@ -42,10 +42,14 @@ class RssmError(RuntimeError):
         self.code = code
 
 
+ROUND_NEAREST, ROUND_STOCHASTIC = 0, 1
+
+
 class Dims(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "batch", "nheads", "headdim", "dstate", "ngroups", "ring_len",
-        "num_slots", "state_dtype", "io_dtype", "out_dtype", "dt_softplus")]
+        "num_slots", "state_dtype", "io_dtype", "out_dtype", "dt_softplus",
+        "rounding")] + [("sr_seed", ctypes.c_uint64), ("sr_offset", ctypes.c_uint64)]
 
 
 class GdnDims(ctypes.Structure):
@@ -126,18 +130,29 @@ def _opt(t, *a, **k):
     return None if t is None else _need(t, *a, **k)
 
 
-def _mamba2_dims(state, x, B, ring_len, y_dtype, dt_softplus):
+def _rounding(rounding):
+    if rounding in ("nearest", None):
+        return ROUND_NEAREST
+    if rounding == "stochastic":
+        return ROUND_STOCHASTIC
+    raise ValueError("rounding must be 'nearest' or 'stochastic'")
+
+
+def _mamba2_dims(state, x, B, ring_len, y_dtype, dt_softplus, rounding=None, sr_seed=0,
+                 sr_offset=0):
     ns, H, P, N = state.shape
     nb = x.shape[0]
     G = B.shape[1]
     if state.dtype not in _DT or x.dtype not in _DT or y_dtype not in _DT:
         raise ValueError("dtypes must be float32 or bfloat16")
     return Dims(nb, H, P, N, G, ring_len, ns, _DT[state.dtype], _DT[x.dtype],
-                _DT[y_dtype], 1 if dt_softplus else 0)
+                _DT[y_dtype], 1 if dt_softplus else 0, _rounding(rounding),
+                sr_seed & (2**64 - 1), sr_offset & (2**64 - 1))
 
 
 def ssu_standard_decode(state, slot_idx, x, dt, A, B, C, D=None, z=None,
                         dt_bias=None, y=None, dt_softplus=True, status=None,
+                        rounding="nearest", sr_seed=0, sr_offset=0,
                         out_dtype=None, stream=None):
     """Standard selective state update (reads and writes ``state``); returns y."""
     dev = _need(state, "state").device
@@ -160,7 +175,7 @@ def ssu_standard_decode(state, slot_idx, x, dt, A, B, C, D=None, z=None,
     if y is None:
         y = torch.empty((nb, H, P), dtype=out_dtype or io, device=dev)
     _need(y, "y", (torch.float32, torch.bfloat16), (nb, H, P), dev=dev)
-    d = _mamba2_dims(state, x, B, 1, y.dtype, dt_softplus)
+    d = _mamba2_dims(state, x, B, 1, y.dtype, dt_softplus, rounding, sr_seed, sr_offset)
     rc = load().ssu_standard_decode(
         ctypes.byref(d), _ptr(state), _ptr(slot_idx), _ptr(x), _ptr(dt), _ptr(A),
         _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(y), _ptr(status),
@@ -172,7 +187,8 @@ def ssu_standard_decode(state, slot_idx, x, dt, A, B, C, D=None, z=None,
 def replayssm_decode(state, x_ring, dt_ring, B_ring, slot_idx, write_pos,
                      is_flush, x, dt, A, B, C, D=None, z=None, dt_bias=None,
                      y=None, next_write_pos=None, next_is_flush=None,
-                     dt_softplus=True, status=None, out_dtype=None, stream=None):
+                     dt_softplus=True, status=None, out_dtype=None, rounding="nearest",
+                     sr_seed=0, sr_offset=0, stream=None):
     """One ReplaySSM output-only decode step; returns y.
 
     Rings: x_ring [slots, H, L, P] (io dtype), dt_ring [slots, H, L] float32,
@@ -209,7 +225,7 @@ def replayssm_decode(state, x_ring, dt_ring, B_ring, slot_idx, write_pos,
     if y is None:
         y = torch.empty((nb, H, P), dtype=out_dtype or io, device=dev)
     _need(y, "y", (torch.float32, torch.bfloat16), (nb, H, P), dev=dev)
-    d = _mamba2_dims(state, x, B, L, y.dtype, dt_softplus)
+    d = _mamba2_dims(state, x, B, L, y.dtype, dt_softplus, rounding, sr_seed, sr_offset)
     rc = load().replayssm_decode(
         ctypes.byref(d), _ptr(state), _ptr(x_ring), _ptr(dt_ring), _ptr(B_ring),
         _ptr(slot_idx), _ptr(write_pos), _ptr(is_flush), _ptr(next_write_pos),
@@ -227,7 +243,7 @@ def replayssm_ring_reset(write_pos, is_flush, rows, ring_len, status=None,
     _need(is_flush, "is_flush", torch.uint8, (nb,), dev=dev)
     _need(rows, "rows", torch.int32, dev=dev)
     _opt(status, "status", torch.int32, (1,))
-    d = Dims(nb, 1, 0, 0, 1, ring_len, 1, 0, 0, 0, 0)
+    d = Dims(nb, 1, 0, 0, 1, ring_len, 1, 0, 0, 0, 0, 0, 0, 0)
     rc = load().replayssm_ring_reset(
         ctypes.byref(d), _ptr(write_pos), _ptr(is_flush), _ptr(rows),
         ctypes.c_int32(rows.numel()), _ptr(status), _stream(stream))

@@ -1,526 +1,16 @@
-// Mamba2 decode kernels for gfx950: the standard selective state update and
-// the ReplaySSM output-only step (checkpoint S0 + per-slot input ring, fold
-// on flush rows only), plus the cursor reset used on slot reuse.
-//
-// Method: vLLM #48018 "[Kernel] ReplaySSM: cache SSM inputs for faster Mamba2
-// standard decode" - Motivation (the per-step state load+store dominates HBM
-// traffic; a ring of inputs plus a periodic checkpoint lets most steps read
-// the output without materialising the state; full write-back once every L
-// steps) and Implementation item 1 (per-row is_flush picks fold+write-back or
-// output only).  The output formula is the recurrence unrolled over the ring
-// window; see the contract in replayssm.h.
-//
-// Mapping: one workgroup per (row, head) tile of the [P, N] state, sized so
-// that every lane streams 16 vectors of 16 bytes (a 16 KB bf16 tile is one
-// wave).  The work is one memory round trip followed by arithmetic:
-//  * row metadata arrives through scalar loads; then every global read of
-//    the step is issued at once: the tile into registers (non-temporal), and
-//    C, z and the w+1 ring rows of x and B straight into LDS with
-//    global_load_lds (no registers, no conversion pass), and dt;
-//  * decay weights come from a wave-wide suffix scan of dt; B_i.C from
-//    16-lane dot products; both stay in lanes and are broadcast with
-//    readlane, so there are no serial LDS loops;
-//  * LPR = N / (elements per vector) adjacent lanes hold one state row; a
-//    butterfly transpose leaves each lane with whole row sums;
-//  * the flush branch depends only on the row, so it is uniform across the
-//    workgroup: flush tiles fold the ring into their registers and store the
-//    new state, the others only read;
-//  * blockIdx is remapped so each XCD works on a contiguous range of rows.
-#include "rssm_device.hpp"
-#include "rssm_host.hpp"
+// Mamba2 decode entry points of the C ABI (standard update, ReplaySSM step,
+// ring reset): argument checks and dispatch to the kernels of
+// mamba2_kernel.hpp.  Stochastic-rounding instances live in mamba2_sr.hip.
+#include <stddef.h>
+
+#include "mamba2_kernel.hpp"
+
+// the Python binding mirrors this layout
+static_assert(sizeof(rssm_dims) == 64 && offsetof(rssm_dims, sr_seed) == 48 &&
+                  offsetof(rssm_dims, sr_offset) == 56,
+              "rssm_dims layout");
 
 namespace rssm {
-
-struct Mamba2Args {
-  void* state;
-  void* x_ring;
-  float* dt_ring;
-  void* B_ring;
-  const int32_t* slot_idx;
-  const int32_t* write_pos;
-  const uint8_t* is_flush;
-  int32_t* next_write_pos;
-  uint8_t* next_is_flush;
-  const void* x;
-  const void* dt;
-  const float* A;
-  const void* B;
-  const void* C;
-  const float* D;
-  const void* z;
-  const float* dt_bias;
-  void* y;
-  int32_t* status;
-  int32_t nheads;
-  int32_t ngroups;
-  int32_t hpg;  // heads per group
-  int32_t ring_len;
-  int32_t num_slots;
-  int32_t dt_softplus;
-};
-
-// Tile geometry.  The replay kernel streams 16 state vectors per lane where
-// the tile allows it (its per-tile staging is amortised over more bytes);
-// the standard update, which also writes every tile, runs 4 per lane (more
-// waves in flight).
-template <typename ST, int P, int N, bool REPLAY>
-struct TileShape {
-  static constexpr int SV = Elt<ST>::kPer16;  // state elements per vector
-  static constexpr int LPR = N / SV;          // lanes per state row
-  static constexpr int NVEC = P * N / SV;     // vectors per tile
-  static constexpr int PER = REPLAY ? 16 : 4; // target vectors per lane
-  static constexpr int NT0 = NVEC / PER;
-  static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 512 ? 512 : NT0);  // threads
-  static constexpr int ITEMS = NVEC / NT;     // vectors per lane
-  static constexpr int RPI = NT / LPR;        // state rows per item
-  // vectors per fold chunk: 32 fp32 accumulators per lane at most
-  static constexpr int ICMAX = 32 / SV;
-  static constexpr int IC = ITEMS < ICMAX ? ITEMS : ICMAX;
-  static constexpr int NCH = ITEMS / IC;            // fold chunks
-  static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "a state row must fit one wave");
-  static_assert(NT % 64 == 0 && NVEC % NT == 0, "whole waves, whole tile");
-  static_assert(ITEMS % IC == 0, "fold chunking");
-};
-
-// LDS staging: 16-byte chunks [C | z | x rows 0..w | B rows 0..w], raw.
-template <typename IT, int P, int N>
-struct Stage {
-  static constexpr int IV = Elt<IT>::kPer16;
-  static constexpr int XV = P / IV;  // chunks per x row
-  static constexpr int BV = N / IV;  // chunks per B / C row
-  static_assert(P % IV == 0 && N % IV == 0, "rows are whole chunks");
-  // ring rows are allocated in multiples of 8 (the dot-product passes)
-  static constexpr int chunks(int L) { return BV + XV + ((L + 7) & ~7) * (XV + BV); }
-};
-
-// Dot product of SV state elements (one 16-byte vector) with the matching C
-// elements held by the lane.  bf16 x bf16 uses the packed dot2 instruction
-// (exact products, fp32 accumulation); otherwise unpack and fma.
-template <typename ST, typename IT, int SV>
-struct RowDot {
-  static constexpr bool kPacked = std::is_same<ST, bf16>::value && std::is_same<IT, bf16>::value;
-  // C held as fp32 (generic) or as packed bf16 pairs
-  float cf[kPacked ? 1 : SV];
-  uint32_t cp[kPacked ? SV / 2 : 1];
-  __device__ inline void load(const char* Cs, int c) {
-    if constexpr (kPacked) {
-      const uint32_t* q = reinterpret_cast<const uint32_t*>(Cs + 2 * c * SV);
-#pragma unroll
-      for (int k = 0; k < SV / 2; ++k) cp[k] = q[k];
-    } else {
-      LdsRead<IT>::template seg<SV>(Cs, c * SV, cf);
-    }
-  }
-  __device__ inline float dot(const u32x4& v) const {
-    float d = 0.f;
-    if constexpr (kPacked) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        // copy the element out first: a bit cast of an ext-vector element
-        // expression reads element 0 whatever the index
-        const uint32_t sk = v[k];
-        const uint32_t ck = cp[k];
-        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, sk),
-                                            __builtin_bit_cast(bf16x2_t, ck), d, false);
-      }
-    } else {
-      float f[SV];
-      Elt<ST>::unpack(v, f);
-#pragma unroll
-      for (int j = 0; j < SV; ++j) d = fmaf(f[j], cf[j], d);
-    }
-    return d;
-  }
-  // C as fp32, for the fold's dot with the new state
-  __device__ inline void cvals(float* out) const {
-    if constexpr (kPacked) {
-#pragma unroll
-      for (int k = 0; k < SV / 2; ++k) {
-        out[2 * k] = __uint_as_float(cp[k] << 16);
-        out[2 * k + 1] = __uint_as_float(cp[k] & 0xffff0000u);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < SV; ++j) out[j] = cf[j];
-    }
-  }
-};
-
-// Fold one chunk of IC state vectors: S_new = cumdecay*S0 + sum_i wt_i x_i B_i
-// for the rows and columns this lane holds; store it; write the row partial
-// sums of S_new . C into part[I0 .. I0+IC).
-template <typename ST, typename IT, int P, int N, int NT, int SV, int IC, int RPI, int ITEMS, int I0>
-__device__ __forceinline__ void fold_chunk(const u32x4 (&raw)[IC], float (&part)[ITEMS], int w,
-                                           float wt, float cumdecay, const char* Bs,
-                                           const char* xs, int c, int prow, const float* cv,
-                                           char* tile, uint32_t lane_off) {
-  float sf[IC][SV];
-#pragma unroll
-  for (int q = 0; q < IC; ++q)
-#pragma unroll
-    for (int j = 0; j < SV; ++j) sf[q][j] = 0.f;
-  // entries in groups of 4; past w the weight is 0 and the row index is
-  // clamped to w, so the extra terms add exact zeros
-  for (int ib = 0; ib <= w; ib += 4) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = ib + k;
-      const int ic = i <= w ? i : w;
-      const float wi = lane_value(wt, i);
-      float bseg[SV];
-      LdsRead<IT>::template seg<SV>(Bs, ic * N + c * SV, bseg);
-#pragma unroll
-      for (int q = 0; q < IC; ++q) {
-        const int p = (I0 + q) * RPI + prow;
-        const float cf = wi * LdsRead<IT>::one(xs, ic * P + p);
-#pragma unroll
-        for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(cf, bseg[j], sf[q][j]);
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < IC; ++q) {
-    float s0[SV];
-    Elt<ST>::unpack(raw[q], s0);
-    float d = 0.f;
-#pragma unroll
-    for (int j = 0; j < SV; ++j) {
-      sf[q][j] = fmaf(cumdecay, s0[j], sf[q][j]);
-      d = fmaf(sf[q][j], cv[j], d);
-    }
-    // keep the row sum here: left alone, the compiler sinks it past the
-    // later chunks and keeps every chunk's accumulators alive until the end
-    asm volatile("" : "+v"(d));
-    part[I0 + q] = d;
-    // Global (not buffer) store: a buffer store with an SGPR offset whose
-    // data registers are rewritten by the next VALU instruction can send the
-    // new value on gfx950, and the compiler only guards the global form.
-    st16_stream(tile, (long)lane_off + (I0 + q) * NT * 16, Elt<ST>::pack(sf[q]));
-  }
-}
-
-struct FoldCtx {
-  int w;
-  float wt, cumdecay;
-  const char* Bs;
-  const char* xs;
-  int c, prow;
-  rsrc_t trs;    // state tile, for the chunk loads
-  char* tile;    // state tile, for the stores
-  uint32_t lane_off;
-};
-
-// Fold chunks CH, CH+1, ... of the tile.  Chunks alternate between the two
-// register buffers; once chunk CH is folded its buffer receives chunk CH+2,
-// so one chunk is always in flight while another is folded.
-template <typename ST, typename IT, int P, int N, int NT, int SV, int IC, int RPI, int ITEMS, int CH>
-__device__ __forceinline__ void fold_from(u32x4 (&ra)[IC], u32x4 (&rb)[IC], float (&part)[ITEMS],
-                                          const float* cv, const FoldCtx& fc) {
-  constexpr int NCH = ITEMS / IC;
-  if constexpr (CH < NCH) {
-    u32x4 (&buf)[IC] = (CH % 2 == 0) ? ra : rb;
-    fold_chunk<ST, IT, P, N, NT, SV, IC, RPI, ITEMS, CH * IC>(buf, part, fc.w, fc.wt, fc.cumdecay,
-                                                             fc.Bs, fc.xs, fc.c, fc.prow, cv,
-                                                             fc.tile, fc.lane_off);
-    if constexpr (CH + 2 < NCH) {
-#pragma unroll
-      for (int q = 0; q < IC; ++q)
-        buf[q] = bload16_nt(fc.trs, fc.lane_off, ((CH + 2) * IC + q) * NT * 16);
-    }
-    fold_from<ST, IT, P, N, NT, SV, IC, RPI, ITEMS, CH + 1>(ra, rb, part, cv, fc);
-  }
-}
-
-template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY>
-__global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
-    mamba2_decode_kernel(const Mamba2Args a) {
-  using TS = TileShape<ST, P, N, REPLAY>;
-  using SG = Stage<IT, P, N>;
-  constexpr int SV = TS::SV, LPR = TS::LPR, NT = TS::NT, ITEMS = TS::ITEMS, RPI = TS::RPI;
-  constexpr int IC = TS::IC, NCH = TS::NCH;
-  constexpr int XV = SG::XV, BV = SG::BV;
-  constexpr long kSt = sizeof(ST);
-  constexpr long kIo = sizeof(IT);
-
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ __attribute__((aligned(16))) float coef_lds[NT];  // ring-term weights per wave
-
-  const int L = REPLAY ? a.ring_len : 1;
-  const int H = a.nheads;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int b = tile / H;
-  const int h = tile - b * H;
-  const int g = h / a.hpg;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  // ---- row metadata (uniform across the workgroup)
-  const int s = a.slot_idx[b];
-  int w = 0;
-  bool f = true;
-  int st = 0;
-  if (REPLAY) {
-    w = a.write_pos[b];
-    f = a.is_flush[b] != 0;
-    if (w < 0 || w >= L) {
-      st |= RSSM_ST_BAD_WRITE_POS;
-      w = w < 0 ? 0 : L - 1;
-      f = true;
-    }
-    if (w == L - 1 && !f) {
-      st |= RSSM_ST_RING_OVERFLOW;
-      f = true;
-    }
-  }
-  const bool bad_slot = s < 0 || s >= a.num_slots;
-  if (bad_slot) st |= RSSM_ST_BAD_SLOT;
-  if (h == 0 && tid == 0) {
-    if (REPLAY) {
-      const int nw = (f || bad_slot) ? 0 : w + 1;
-      if (a.next_write_pos) a.next_write_pos[b] = nw;
-      if (a.next_is_flush) a.next_is_flush[b] = (nw == L - 1) ? 1 : 0;
-    }
-    if (st && a.status) atomicOr(a.status, st);
-  }
-  const long yoff = ((long)b * H + h) * P;
-  if (bad_slot) {
-    for (int p = tid; p < P; p += NT) Elt<OT>::store1(a.y, yoff + p, __builtin_nanf(""));
-    return;
-  }
-
-  char* const tptr = (char*)a.state + ((long)s * H + h) * (long)P * N * kSt;
-  const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(P * N * kSt));
-  const uint32_t lane_off = tid * 16;
-  const long xcur = yoff;                                // x[b, h, :]
-  const long bccur = ((long)b * a.ngroups + g) * N;      // B, C[b, g, :]
-  const long xring0 = ((long)s * H + h) * (long)L * P;   // x_ring[s, h, 0, :]
-  const long bring0 = ((long)s * a.ngroups + g) * (long)L * N;
-  const long dtring0 = ((long)s * H + h) * L;
-  const int nZ = a.z ? XV : 0;
-  const int oX = BV + nZ;                // first chunk of the x rows
-  const int oB = oX + (w + 1) * XV;      // first chunk of the B rows
-  const int nAll = oB + (w + 1) * BV;
-
-  // Stage C, z, x_0..x_w, B_0..B_w (entry w = the current step) into LDS
-  // with direct-to-LDS loads, one contiguous global span at a time (the w
-  // ring rows of a slot are contiguous), and load dt of entries 0..w (lane i).
-  // span: LDS chunks [c0, c0+n); the first nring from `ring`, then `cur`.
-  auto dma_span = [&](int c0, int n, const char* ring, int nring, const char* cur) {
-    for (int j = wave * 64; j < n; j += NT) {
-      const int u = j + lane;
-      if (u < n) {
-        const char* src = u < nring ? ring + (long)u * 16 : cur + (long)(u - nring) * 16;
-        dma16(src, lds + (long)(c0 + j) * 16);
-      }
-    }
-  };
-  auto stage = [&]() {
-    if constexpr (!REPLAY) {
-      // no ring: C, z, x, B are at most a few dozen chunks, one per lane
-      for (int u = tid; u < nAll; u += NT) {
-        const char* src;
-        if (u < BV) src = (const char*)a.C + (bccur * kIo + (long)u * 16);
-        else if (u < oX) src = (const char*)a.z + (xcur * kIo + (long)(u - BV) * 16);
-        else if (u < oB) src = (const char*)a.x + (xcur * kIo + (long)(u - oX) * 16);
-        else src = (const char*)a.B + (bccur * kIo + (long)(u - oB) * 16);
-        dma16(src, lds + (long)(u - lane) * 16);
-      }
-      return;
-    }
-    const char* cg = (const char*)a.C + bccur * kIo;
-    dma_span(0, BV, cg, BV, cg);
-    if (a.z) {
-      const char* zg = (const char*)a.z + xcur * kIo;
-      dma_span(BV, XV, zg, XV, zg);
-    }
-    dma_span(oX, (w + 1) * XV, REPLAY ? (const char*)a.x_ring + xring0 * kIo : nullptr,
-             REPLAY ? w * XV : 0, (const char*)a.x + xcur * kIo);
-    dma_span(oB, (w + 1) * BV, REPLAY ? (const char*)a.B_ring + bring0 * kIo : nullptr,
-             REPLAY ? w * BV : 0, (const char*)a.B + bccur * kIo);
-  };
-  // dt of entries 0..w (lane i): the loads are issued after the tile reads
-  // (load_dt), the bias and softplus applied after the wait (finish_dt), so
-  // no scalar round trip sits in front of the tile stream.
-  float dti = 0.f, dtr = 0.f, dtb = 0.f;
-  auto load_dt = [&]() {
-    if (REPLAY && lane < w) dti = a.dt_ring[dtring0 + lane];
-    dtr = Elt<IT>::load1(a.dt, (long)b * H + h);
-    if (a.dt_bias) dtb = a.dt_bias[h];
-  };
-  auto finish_dt = [&]() {
-    const float v = dtr + dtb;
-    const float dcur = a.dt_softplus ? softplus_f32(v) : v;
-    if (lane == w) dti = dcur;
-  };
-  const float Ah = a.A[h];
-  const float Dh = a.D ? a.D[h] : 0.f;
-
-  const char* Cs = lds;
-  const char* zs = lds + BV * 16;
-  const char* xs = lds + oX * 16;
-  const char* Bs = lds + (long)oB * 16;
-  const int c = tid % LPR;
-  const int prow = tid / LPR;
-
-  float part[ITEMS];
-  float cumdecay, coef = 0.f;  // coef (lane i): wt_i * (B_i . C), output-only rows
-  if (!f) {
-    // ================= output-only tile: the whole tile in flight at once
-    u32x4 sv[ITEMS];
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
-    stage();
-    load_dt();
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    finish_dt();
-    // append the current step at ring position w (replay only: the standard
-    // update has no ring and never reaches this branch)
-    if (REPLAY && wave == 0) {
-      const bool b_writer = (h % a.hpg) == 0;  // one writer per group
-      for (int k = lane; k < XV + BV; k += 64) {
-        if (k < XV) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(xs + ((long)w * XV + k) * 16);
-          st16(a.x_ring, ((xring0 + (long)w * P) * kIo) + k * 16, v);
-        } else if (b_writer) {
-          const int cb = k - XV;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + ((long)w * BV + cb) * 16);
-          st16(a.B_ring, ((bring0 + (long)w * N) * kIo) + cb * 16, v);
-        }
-      }
-      if (lane == w) a.dt_ring[dtring0 + w] = dti;
-    }
-    // decay weights: wt_i = dt_i * exp(A * sum_{i<j<=w} dt_j)
-    const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
-    cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
-    const float wt = lane <= w ? dti * expf(Ah * rsuf) : 0.f;
-    // B_i . C: 8 lanes per dot, 8 dots per pass
-    {
-      constexpr int EPL = N / 8;
-      const int q8 = lane & 7;
-      float cpart[EPL];
-      LdsRead<IT>::template seg<EPL>(Cs, q8 * EPL, cpart);
-      float bc = 0.f;
-#pragma unroll 2
-      for (int q = 0; q * 8 <= w; ++q) {
-        const int i = q * 8 + (lane >> 3);
-        float bv[EPL];
-        LdsRead<IT>::template seg<EPL>(Bs, i * N + q8 * EPL, bv);
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(bv[e], cpart[e], acc);
-        acc = group_sum<8>(acc);
-        const float t = __shfl(acc, (lane & 7) * 8, 64);
-        if ((lane >> 3) == q) bc = t;
-      }
-      coef = lane <= w ? wt * bc : 0.f;
-      coef_lds[wave * 64 + lane] = coef;  // broadcast to the wave through LDS
-      __builtin_amdgcn_wave_barrier();
-    }
-    // S0 . C per state row
-    RowDot<ST, IT, SV> rd;
-    rd.load(Cs, c);
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) part[it] = rd.dot(sv[it]);
-  } else {
-    // ================= flush tile: stream the tile in chunks, fold, store
-    u32x4 ra[IC], rb[IC];
-#pragma unroll
-    for (int q = 0; q < IC; ++q) ra[q] = bload16_nt(trs, lane_off, q * NT * 16);
-    if constexpr (NCH > 1) {
-#pragma unroll
-      for (int q = 0; q < IC; ++q) rb[q] = bload16_nt(trs, lane_off, (IC + q) * NT * 16);
-    }
-    stage();
-    load_dt();
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    finish_dt();
-    const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
-    cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
-    const float wt = lane <= w ? dti * expf(Ah * rsuf) : 0.f;
-    RowDot<ST, IT, SV> rd;
-    rd.load(Cs, c);
-    float cv[SV];
-    rd.cvals(cv);
-    FoldCtx fc{w, wt, cumdecay, Bs, xs, c, prow, trs, tptr, lane_off};
-    fold_from<ST, IT, P, N, NT, SV, IC, RPI, ITEMS, 0>(ra, rb, part, cv, fc);
-  }
-
-  // ---- whole rows per lane; ring term, D*x, gate, store
-  using RR = RowReduce<ITEMS, LPR>;
-  RR::run(part, tid);
-  const bool writer = (c % RR::DUP) == 0;
-#pragma unroll
-  for (int j = 0; j < RR::NF; ++j) {
-    const int p = RR::item(j, tid) * RPI + prow;
-    float yv = part[j];
-    if (!f) {
-      // coef is 0 past w; row indexes are clamped to w
-      yv *= cumdecay;
-      const float* cw = coef_lds + wave * 64;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        yv = fmaf(cw[i], LdsRead<IT>::one(xs, (i <= w ? i : w) * P + p), yv);
-      for (int i = 16; i <= w; ++i) yv = fmaf(cw[i], LdsRead<IT>::one(xs, i * P + p), yv);
-    }
-    yv = fmaf(Dh, LdsRead<IT>::one(xs, w * P + p), yv);
-    if (a.z) yv = silu_gate(yv, LdsRead<IT>::one(zs, p));
-    if (writer) Elt<OT>::store1(a.y, yoff + p, yv);
-  }
-}
-
-template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY>
-static int launch_mamba2(const Mamba2Args& a, int batch, hipStream_t stream) {
-  using TS = TileShape<ST, P, N, REPLAY>;
-  const int L = REPLAY ? a.ring_len : 1;  // L <= 64: one dt per lane of a wave
-  const size_t lds = (size_t)Stage<IT, P, N>::chunks(L) * 16;
-  if (lds > kMaxLds) return RSSM_ESHAPE;  // ring rows must fit one workgroup's LDS
-  const long grid = (long)batch * a.nheads;
-  return launch_kernel(
-      reinterpret_cast<const void*>(&mamba2_decode_kernel<ST, IT, OT, P, N, REPLAY>),
-      (unsigned)grid, TS::NT, lds, stream, a);
-}
-
-template <bool REPLAY, typename ST, typename IT, typename OT>
-static int dispatch_shape(const Mamba2Args& a, const rssm_dims& d, hipStream_t s) {
-#define RSSM_SHAPE(PP, NN) \
-  if (d.headdim == PP && d.dstate == NN) return launch_mamba2<ST, IT, OT, PP, NN, REPLAY>(a, d.batch, s);
-  RSSM_SHAPE(64, 128)
-  RSSM_SHAPE(64, 16)
-  RSSM_SHAPE(64, 32)
-  RSSM_SHAPE(64, 64)
-  RSSM_SHAPE(64, 256)
-  RSSM_SHAPE(32, 16)
-  RSSM_SHAPE(32, 32)
-  RSSM_SHAPE(32, 64)
-  RSSM_SHAPE(32, 128)
-  RSSM_SHAPE(32, 256)
-  RSSM_SHAPE(128, 16)
-  RSSM_SHAPE(128, 32)
-  RSSM_SHAPE(128, 64)
-  RSSM_SHAPE(128, 128)
-  RSSM_SHAPE(128, 256)
-#undef RSSM_SHAPE
-  return RSSM_ESHAPE;
-}
-
-template <bool REPLAY>
-static int dispatch_mamba2(const Mamba2Args& a, const rssm_dims& d, hipStream_t s) {
-  const int key = d.state_dtype * 4 + d.io_dtype * 2 + d.out_dtype;
-  switch (key) {
-    case 0: return dispatch_shape<REPLAY, float, float, float>(a, d, s);
-    case 1: return dispatch_shape<REPLAY, float, float, bf16>(a, d, s);
-    case 2: return dispatch_shape<REPLAY, float, bf16, float>(a, d, s);
-    case 3: return dispatch_shape<REPLAY, float, bf16, bf16>(a, d, s);
-    case 4: return dispatch_shape<REPLAY, bf16, float, float>(a, d, s);
-    case 5: return dispatch_shape<REPLAY, bf16, float, bf16>(a, d, s);
-    case 6: return dispatch_shape<REPLAY, bf16, bf16, float>(a, d, s);
-    case 7: return dispatch_shape<REPLAY, bf16, bf16, bf16>(a, d, s);
-  }
-  return RSSM_EDTYPE;
-}
 
 static bool shape_supported(int P, int N) {
   const bool p_ok = P == 32 || P == 64 || P == 128;
@@ -538,7 +28,15 @@ static int check_dims(const rssm_dims* d, bool replay) {
     return RSSM_EDTYPE;
   if (!shape_supported(d->headdim, d->dstate)) return RSSM_ESHAPE;
   if (replay && (d->ring_len < 1 || d->ring_len > 64)) return RSSM_ESHAPE;
+  if (d->rounding != RSSM_ROUND_NEAREST && d->rounding != RSSM_ROUND_STOCHASTIC)
+    return RSSM_EINVAL;
+  if (d->rounding == RSSM_ROUND_STOCHASTIC && d->state_dtype != RSSM_BF16) return RSSM_EDTYPE;
   return RSSM_OK;
+}
+
+static int dispatch(bool replay, const Mamba2Args& a, const rssm_dims& d, hipStream_t s) {
+  if (d.rounding == RSSM_ROUND_STOCHASTIC) return dispatch_mamba2_sr(replay, a, d, s);
+  return replay ? dispatch_mamba2<true, false>(a, d, s) : dispatch_mamba2<false, false>(a, d, s);
 }
 
 }  // namespace rssm
@@ -576,7 +74,9 @@ extern "C" int ssu_standard_decode(const rssm_dims* dims, void* state, const int
   a.ring_len = 1;
   a.num_slots = dims->num_slots;
   a.dt_softplus = dims->dt_softplus;
-  return dispatch_mamba2<false>(a, *dims, stream);
+  a.sr_seed = dims->sr_seed;
+  a.sr_offset = dims->sr_offset;
+  return dispatch(false, a, *dims, stream);
 }
 
 extern "C" int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring, float* dt_ring,
@@ -623,7 +123,9 @@ extern "C" int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring
   a.ring_len = dims->ring_len;
   a.num_slots = dims->num_slots;
   a.dt_softplus = dims->dt_softplus;
-  return dispatch_mamba2<true>(a, *dims, stream);
+  a.sr_seed = dims->sr_seed;
+  a.sr_offset = dims->sr_offset;
+  return dispatch(true, a, *dims, stream);
 }
 
 namespace rssm {
@@ -675,4 +177,4 @@ extern "C" const char* replayssm_strerror(int code) {
   return "unknown error";
 }
 
-extern "C" int replayssm_abi_version(void) { return 100; }
+extern "C" int replayssm_abi_version(void) { return 101; }

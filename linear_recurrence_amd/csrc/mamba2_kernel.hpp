@@ -1,0 +1,597 @@
+// Mamba2 decode kernels for gfx950: the standard selective state update and
+// the ReplaySSM output-only step (checkpoint S0 + per-slot input ring, fold
+// on flush rows only), plus the cursor reset used on slot reuse.
+//
+// Method: vLLM #48018 "[Kernel] ReplaySSM: cache SSM inputs for faster Mamba2
+// standard decode" - Motivation (the per-step state load+store dominates HBM
+// traffic; a ring of inputs plus a periodic checkpoint lets most steps read
+// the output without materialising the state; full write-back once every L
+// steps) and Implementation item 1 (per-row is_flush picks fold+write-back or
+// output only).  The output formula is the recurrence unrolled over the ring
+// window; see the contract in replayssm.h.
+//
+// Mapping: one workgroup per (row, head) tile of the [P, N] state, sized so
+// that every lane streams 16 vectors of 16 bytes (a 16 KB bf16 tile is one
+// wave).  The work is one memory round trip followed by arithmetic:
+//  * row metadata arrives through scalar loads; then every global read of
+//    the step is issued at once: the tile into registers (non-temporal), and
+//    C, z and the w+1 ring rows of x and B straight into LDS with
+//    global_load_lds (no registers, no conversion pass), and dt;
+//  * decay weights come from a wave-wide suffix scan of dt; B_i.C from
+//    16-lane dot products; both stay in lanes and are broadcast with
+//    readlane, so there are no serial LDS loops;
+//  * LPR = N / (elements per vector) adjacent lanes hold one state row; a
+//    butterfly transpose leaves each lane with whole row sums;
+//  * the flush branch depends only on the row, so it is uniform across the
+//    workgroup: flush tiles fold the ring into their registers and store the
+//    new state, the others only read;
+//  * blockIdx is remapped so each XCD works on a contiguous range of rows.
+#pragma once
+
+#include "rssm_device.hpp"
+#include "rssm_host.hpp"
+
+namespace rssm {
+
+struct Mamba2Args {
+  void* state;
+  void* x_ring;
+  float* dt_ring;
+  void* B_ring;
+  const int32_t* slot_idx;
+  const int32_t* write_pos;
+  const uint8_t* is_flush;
+  int32_t* next_write_pos;
+  uint8_t* next_is_flush;
+  const void* x;
+  const void* dt;
+  const float* A;
+  const void* B;
+  const void* C;
+  const float* D;
+  const void* z;
+  const float* dt_bias;
+  void* y;
+  int32_t* status;
+  int32_t nheads;
+  int32_t ngroups;
+  int32_t hpg;  // heads per group
+  int32_t ring_len;
+  int32_t num_slots;
+  int32_t dt_softplus;
+  uint64_t sr_seed;    // stochastic rounding: Philox key (seed, offset)
+  uint64_t sr_offset;
+};
+
+// Tile geometry.  The replay kernel streams 16 state vectors per lane where
+// the tile allows it (its per-tile staging is amortised over more bytes);
+// the standard update, which also writes every tile, runs 4 per lane (more
+// waves in flight).
+template <typename ST, int P, int N, bool REPLAY>
+struct TileShape {
+  static constexpr int SV = Elt<ST>::kPer16;  // state elements per vector
+  static constexpr int LPR = N / SV;          // lanes per state row
+  static constexpr int NVEC = P * N / SV;     // vectors per tile
+  static constexpr int PER = REPLAY ? 16 : 4; // target vectors per lane
+  static constexpr int NT0 = NVEC / PER;
+  static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 512 ? 512 : NT0);  // threads
+  static constexpr int ITEMS = NVEC / NT;     // vectors per lane
+  static constexpr int RPI = NT / LPR;        // state rows per item
+  // vectors per fold chunk: 32 fp32 accumulators per lane at most
+  static constexpr int ICMAX = 32 / SV;
+  static constexpr int IC = ITEMS < ICMAX ? ITEMS : ICMAX;
+  static constexpr int NCH = ITEMS / IC;            // fold chunks
+  static_assert(LPR >= 1 && LPR <= 64 && 64 % LPR == 0, "a state row must fit one wave");
+  static_assert(NT % 64 == 0 && NVEC % NT == 0, "whole waves, whole tile");
+  static_assert(ITEMS % IC == 0, "fold chunking");
+};
+
+// LDS staging: 16-byte chunks [C | z | x rows 0..w | B rows 0..w], raw.
+template <typename IT, int P, int N>
+struct Stage {
+  static constexpr int IV = Elt<IT>::kPer16;
+  static constexpr int XV = P / IV;  // chunks per x row
+  static constexpr int BV = N / IV;  // chunks per B / C row
+  static_assert(P % IV == 0 && N % IV == 0, "rows are whole chunks");
+  // ring rows are allocated in multiples of 8 (the dot-product passes)
+  static constexpr int chunks(int L) { return BV + XV + ((L + 7) & ~7) * (XV + BV); }
+};
+
+// Dot product of SV state elements (one 16-byte vector) with the matching C
+// elements held by the lane.  bf16 x bf16 uses the packed dot2 instruction
+// (exact products, fp32 accumulation); otherwise unpack and fma.
+template <typename ST, typename IT, int SV>
+struct RowDot {
+  static constexpr bool kPacked = std::is_same<ST, bf16>::value && std::is_same<IT, bf16>::value;
+  // C held as fp32 (generic) or as packed bf16 pairs
+  float cf[kPacked ? 1 : SV];
+  uint32_t cp[kPacked ? SV / 2 : 1];
+  __device__ inline void load(const char* Cs, int c) {
+    if constexpr (kPacked) {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(Cs + 2 * c * SV);
+#pragma unroll
+      for (int k = 0; k < SV / 2; ++k) cp[k] = q[k];
+    } else {
+      LdsRead<IT>::template seg<SV>(Cs, c * SV, cf);
+    }
+  }
+  __device__ inline float dot(const u32x4& v) const {
+    float d = 0.f;
+    if constexpr (kPacked) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // copy the element out first: a bit cast of an ext-vector element
+        // expression reads element 0 whatever the index
+        const uint32_t sk = v[k];
+        const uint32_t ck = cp[k];
+        d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, sk),
+                                            __builtin_bit_cast(bf16x2_t, ck), d, false);
+      }
+    } else {
+      float f[SV];
+      Elt<ST>::unpack(v, f);
+#pragma unroll
+      for (int j = 0; j < SV; ++j) d = fmaf(f[j], cf[j], d);
+    }
+    return d;
+  }
+  // C as fp32, for the fold's dot with the new state
+  __device__ inline void cvals(float* out) const {
+    if constexpr (kPacked) {
+#pragma unroll
+      for (int k = 0; k < SV / 2; ++k) {
+        out[2 * k] = __uint_as_float(cp[k] << 16);
+        out[2 * k + 1] = __uint_as_float(cp[k] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SV; ++j) out[j] = cf[j];
+    }
+  }
+};
+
+// Fold one chunk of IC state vectors: S_new = cumdecay*S0 + sum_i wt_i x_i B_i
+// for the rows and columns this lane holds; store it; write the row partial
+// sums of S_new . C into part[I0 .. I0+IC).
+// Stochastic rounding of the bf16 write-back.  The random bits of element
+// e of a tile come from Philox4x64-10 with key (seed, offset) and counter
+// (tile * (P*N/16) + e/16, 0, 0, 0), where tile = slot * nheads + head:
+// element e uses bits 16*(e%4) .. of output word (e%16)/4.  One call covers
+// 16 consecutive elements, i.e. the 16-byte vectors of two adjacent lanes.
+struct SrCtx {
+  uint64_t k0, k1;   // key
+  uint64_t blk0;     // counter of the tile's first 16 elements
+};
+
+template <typename ST, int NT, int IC, int I0, bool SR>
+__device__ __forceinline__ void store_chunk(float (&sf)[IC][Elt<ST>::kPer16], char* tile,
+                                            uint32_t lane_off, const SrCtx& sr) {
+  if constexpr (!SR) {
+#pragma unroll
+    for (int q = 0; q < IC; ++q)
+      st16_stream(tile, (long)lane_off + (I0 + q) * NT * 16, Elt<ST>::pack(sf[q]));
+  } else {
+    static_assert(std::is_same<ST, bf16>::value, "stochastic rounding targets bf16 state");
+    const int tid = threadIdx.x;
+    const int par = tid & 1;  // vector v = item*NT + tid is half v%2 of block v/2
+    if constexpr (IC % 2 == 0) {
+      // lanes of a pair each draw one block: the even lane the block of item
+      // q, the odd lane that of item q+1, and trade the halves they lack
+#pragma unroll
+      for (int q = 0; q < IC; q += 2) {
+        uint64_t c[4] = {sr.blk0 + (uint64_t)((((I0 + q + par) * NT) + tid) >> 1), 0, 0, 0};
+        philox4x64_10(c, sr.k0, sr.k1);
+        const uint64_t keep0 = par ? c[2] : c[0], keep1 = par ? c[3] : c[1];
+        const uint64_t got0 = swap_lane_pair(par ? c[0] : c[2]);
+        const uint64_t got1 = swap_lane_pair(par ? c[1] : c[3]);
+        const u32x4 va = par ? bf16_pack_sr(sf[q], got0, got1) : bf16_pack_sr(sf[q], keep0, keep1);
+        const u32x4 vb =
+            par ? bf16_pack_sr(sf[q + 1], keep0, keep1) : bf16_pack_sr(sf[q + 1], got0, got1);
+        st16_stream(tile, (long)lane_off + (I0 + q) * NT * 16, va);
+        st16_stream(tile, (long)lane_off + (I0 + q + 1) * NT * 16, vb);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < IC; ++q) {
+        uint64_t c[4] = {sr.blk0 + (uint64_t)((((I0 + q) * NT) + tid) >> 1), 0, 0, 0};
+        philox4x64_10(c, sr.k0, sr.k1);
+        const u32x4 v = par ? bf16_pack_sr(sf[q], c[2], c[3]) : bf16_pack_sr(sf[q], c[0], c[1]);
+        st16_stream(tile, (long)lane_off + (I0 + q) * NT * 16, v);
+      }
+    }
+  }
+}
+
+template <typename ST, typename IT, int P, int N, int NT, int SV, int IC, int RPI, int ITEMS, int I0,
+          bool SR>
+__device__ __forceinline__ void fold_chunk(const u32x4 (&raw)[IC], float (&part)[ITEMS], int w,
+                                           float wt, float cumdecay, const char* Bs,
+                                           const char* xs, int c, int prow, const float* cv,
+                                           char* tile, uint32_t lane_off, const SrCtx& sr) {
+  float sf[IC][SV];
+#pragma unroll
+  for (int q = 0; q < IC; ++q)
+#pragma unroll
+    for (int j = 0; j < SV; ++j) sf[q][j] = 0.f;
+  // entries in groups of 4; past w the weight is 0 and the row index is
+  // clamped to w, so the extra terms add exact zeros
+  for (int ib = 0; ib <= w; ib += 4) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = ib + k;
+      const int ic = i <= w ? i : w;
+      const float wi = lane_value(wt, i);
+      float bseg[SV];
+      LdsRead<IT>::template seg<SV>(Bs, ic * N + c * SV, bseg);
+#pragma unroll
+      for (int q = 0; q < IC; ++q) {
+        const int p = (I0 + q) * RPI + prow;
+        const float cf = wi * LdsRead<IT>::one(xs, ic * P + p);
+#pragma unroll
+        for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(cf, bseg[j], sf[q][j]);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < IC; ++q) {
+    float s0[SV];
+    Elt<ST>::unpack(raw[q], s0);
+    float d = 0.f;
+#pragma unroll
+    for (int j = 0; j < SV; ++j) {
+      sf[q][j] = fmaf(cumdecay, s0[j], sf[q][j]);
+      d = fmaf(sf[q][j], cv[j], d);
+    }
+    // keep the row sum here: left alone, the compiler sinks it past the
+    // later chunks and keeps every chunk's accumulators alive until the end
+    asm volatile("" : "+v"(d));
+    part[I0 + q] = d;
+  }
+  // Global (not buffer) stores: a buffer store with an SGPR offset whose
+  // data registers are rewritten by the next VALU instruction can send the
+  // new value on gfx950, and the compiler only guards the global form.
+  store_chunk<ST, NT, IC, I0, SR>(sf, tile, lane_off, sr);
+}
+
+struct FoldCtx {
+  int w;
+  float wt, cumdecay;
+  const char* Bs;
+  const char* xs;
+  int c, prow;
+  rsrc_t trs;    // state tile, for the chunk loads
+  char* tile;    // state tile, for the stores
+  uint32_t lane_off;
+  SrCtx sr;
+};
+
+// Fold chunks CH, CH+1, ... of the tile.  Chunks alternate between the two
+// register buffers; once chunk CH is folded its buffer receives chunk CH+2,
+// so one chunk is always in flight while another is folded.
+template <typename ST, typename IT, int P, int N, int NT, int SV, int IC, int RPI, int ITEMS, int CH,
+          bool SR>
+__device__ __forceinline__ void fold_from(u32x4 (&ra)[IC], u32x4 (&rb)[IC], float (&part)[ITEMS],
+                                          const float* cv, const FoldCtx& fc) {
+  constexpr int NCH = ITEMS / IC;
+  if constexpr (CH < NCH) {
+    u32x4 (&buf)[IC] = (CH % 2 == 0) ? ra : rb;
+    fold_chunk<ST, IT, P, N, NT, SV, IC, RPI, ITEMS, CH * IC, SR>(
+        buf, part, fc.w, fc.wt, fc.cumdecay, fc.Bs, fc.xs, fc.c, fc.prow, cv, fc.tile,
+        fc.lane_off, fc.sr);
+    if constexpr (CH + 2 < NCH) {
+#pragma unroll
+      for (int q = 0; q < IC; ++q)
+        buf[q] = bload16_nt(fc.trs, fc.lane_off, ((CH + 2) * IC + q) * NT * 16);
+    }
+    fold_from<ST, IT, P, N, NT, SV, IC, RPI, ITEMS, CH + 1, SR>(ra, rb, part, cv, fc);
+  }
+}
+
+template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY, bool SR>
+__global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
+    mamba2_decode_kernel(const Mamba2Args a) {
+  using TS = TileShape<ST, P, N, REPLAY>;
+  using SG = Stage<IT, P, N>;
+  constexpr int SV = TS::SV, LPR = TS::LPR, NT = TS::NT, ITEMS = TS::ITEMS, RPI = TS::RPI;
+  constexpr int IC = TS::IC, NCH = TS::NCH;
+  constexpr int XV = SG::XV, BV = SG::BV;
+  constexpr long kSt = sizeof(ST);
+  constexpr long kIo = sizeof(IT);
+
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ __attribute__((aligned(16))) float coef_lds[NT];  // ring-term weights per wave
+
+  const int L = REPLAY ? a.ring_len : 1;
+  const int H = a.nheads;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int b = tile / H;
+  const int h = tile - b * H;
+  const int g = h / a.hpg;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // ---- row metadata (uniform across the workgroup)
+  const int s = a.slot_idx[b];
+  int w = 0;
+  bool f = true;
+  int st = 0;
+  if (REPLAY) {
+    w = a.write_pos[b];
+    f = a.is_flush[b] != 0;
+    if (w < 0 || w >= L) {
+      st |= RSSM_ST_BAD_WRITE_POS;
+      w = w < 0 ? 0 : L - 1;
+      f = true;
+    }
+    if (w == L - 1 && !f) {
+      st |= RSSM_ST_RING_OVERFLOW;
+      f = true;
+    }
+  }
+  const bool bad_slot = s < 0 || s >= a.num_slots;
+  if (bad_slot) st |= RSSM_ST_BAD_SLOT;
+  if (h == 0 && tid == 0) {
+    if (REPLAY) {
+      const int nw = (f || bad_slot) ? 0 : w + 1;
+      if (a.next_write_pos) a.next_write_pos[b] = nw;
+      if (a.next_is_flush) a.next_is_flush[b] = (nw == L - 1) ? 1 : 0;
+    }
+    if (st && a.status) atomicOr(a.status, st);
+  }
+  const long yoff = ((long)b * H + h) * P;
+  if (bad_slot) {
+    for (int p = tid; p < P; p += NT) Elt<OT>::store1(a.y, yoff + p, __builtin_nanf(""));
+    return;
+  }
+
+  char* const tptr = (char*)a.state + ((long)s * H + h) * (long)P * N * kSt;
+  const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(P * N * kSt));
+  const uint32_t lane_off = tid * 16;
+  const long xcur = yoff;                                // x[b, h, :]
+  const long bccur = ((long)b * a.ngroups + g) * N;      // B, C[b, g, :]
+  const long xring0 = ((long)s * H + h) * (long)L * P;   // x_ring[s, h, 0, :]
+  const long bring0 = ((long)s * a.ngroups + g) * (long)L * N;
+  const long dtring0 = ((long)s * H + h) * L;
+  const int nZ = a.z ? XV : 0;
+  const int oX = BV + nZ;                // first chunk of the x rows
+  const int oB = oX + (w + 1) * XV;      // first chunk of the B rows
+  const int nAll = oB + (w + 1) * BV;
+
+  // Stage C, z, x_0..x_w, B_0..B_w (entry w = the current step) into LDS
+  // with direct-to-LDS loads, one contiguous global span at a time (the w
+  // ring rows of a slot are contiguous), and load dt of entries 0..w (lane i).
+  // span: LDS chunks [c0, c0+n); the first nring from `ring`, then `cur`.
+  auto dma_span = [&](int c0, int n, const char* ring, int nring, const char* cur) {
+    for (int j = wave * 64; j < n; j += NT) {
+      const int u = j + lane;
+      if (u < n) {
+        const char* src = u < nring ? ring + (long)u * 16 : cur + (long)(u - nring) * 16;
+        dma16(src, lds + (long)(c0 + j) * 16);
+      }
+    }
+  };
+  auto stage = [&]() {
+    if constexpr (!REPLAY) {
+      // no ring: C, z, x, B are at most a few dozen chunks, one per lane
+      for (int u = tid; u < nAll; u += NT) {
+        const char* src;
+        if (u < BV) src = (const char*)a.C + (bccur * kIo + (long)u * 16);
+        else if (u < oX) src = (const char*)a.z + (xcur * kIo + (long)(u - BV) * 16);
+        else if (u < oB) src = (const char*)a.x + (xcur * kIo + (long)(u - oX) * 16);
+        else src = (const char*)a.B + (bccur * kIo + (long)(u - oB) * 16);
+        dma16(src, lds + (long)(u - lane) * 16);
+      }
+      return;
+    }
+    const char* cg = (const char*)a.C + bccur * kIo;
+    dma_span(0, BV, cg, BV, cg);
+    if (a.z) {
+      const char* zg = (const char*)a.z + xcur * kIo;
+      dma_span(BV, XV, zg, XV, zg);
+    }
+    dma_span(oX, (w + 1) * XV, REPLAY ? (const char*)a.x_ring + xring0 * kIo : nullptr,
+             REPLAY ? w * XV : 0, (const char*)a.x + xcur * kIo);
+    dma_span(oB, (w + 1) * BV, REPLAY ? (const char*)a.B_ring + bring0 * kIo : nullptr,
+             REPLAY ? w * BV : 0, (const char*)a.B + bccur * kIo);
+  };
+  // dt of entries 0..w (lane i): the loads are issued after the tile reads
+  // (load_dt), the bias and softplus applied after the wait (finish_dt), so
+  // no scalar round trip sits in front of the tile stream.
+  float dti = 0.f, dtr = 0.f, dtb = 0.f;
+  auto load_dt = [&]() {
+    if (REPLAY && lane < w) dti = a.dt_ring[dtring0 + lane];
+    dtr = Elt<IT>::load1(a.dt, (long)b * H + h);
+    if (a.dt_bias) dtb = a.dt_bias[h];
+  };
+  auto finish_dt = [&]() {
+    const float v = dtr + dtb;
+    const float dcur = a.dt_softplus ? softplus_f32(v) : v;
+    if (lane == w) dti = dcur;
+  };
+  const float Ah = a.A[h];
+  const float Dh = a.D ? a.D[h] : 0.f;
+
+  const char* Cs = lds;
+  const char* zs = lds + BV * 16;
+  const char* xs = lds + oX * 16;
+  const char* Bs = lds + (long)oB * 16;
+  const int c = tid % LPR;
+  const int prow = tid / LPR;
+
+  float part[ITEMS];
+  float cumdecay, coef = 0.f;  // coef (lane i): wt_i * (B_i . C), output-only rows
+  if (!f) {
+    // ================= output-only tile: the whole tile in flight at once
+    u32x4 sv[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
+    stage();
+    load_dt();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    finish_dt();
+    // append the current step at ring position w (replay only: the standard
+    // update has no ring and never reaches this branch)
+    if (REPLAY && wave == 0) {
+      const bool b_writer = (h % a.hpg) == 0;  // one writer per group
+      for (int k = lane; k < XV + BV; k += 64) {
+        if (k < XV) {
+          const u32x4 v = *reinterpret_cast<const u32x4*>(xs + ((long)w * XV + k) * 16);
+          st16(a.x_ring, ((xring0 + (long)w * P) * kIo) + k * 16, v);
+        } else if (b_writer) {
+          const int cb = k - XV;
+          const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + ((long)w * BV + cb) * 16);
+          st16(a.B_ring, ((bring0 + (long)w * N) * kIo) + cb * 16, v);
+        }
+      }
+      if (lane == w) a.dt_ring[dtring0 + w] = dti;
+    }
+    // decay weights: wt_i = dt_i * exp(A * sum_{i<j<=w} dt_j)
+    const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
+    cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
+    const float wt = lane <= w ? dti * expf(Ah * rsuf) : 0.f;
+    // B_i . C: 8 lanes per dot, 8 dots per pass
+    {
+      constexpr int EPL = N / 8;
+      const int q8 = lane & 7;
+      float cpart[EPL];
+      LdsRead<IT>::template seg<EPL>(Cs, q8 * EPL, cpart);
+      float bc = 0.f;
+#pragma unroll 2
+      for (int q = 0; q * 8 <= w; ++q) {
+        const int i = q * 8 + (lane >> 3);
+        float bv[EPL];
+        LdsRead<IT>::template seg<EPL>(Bs, i * N + q8 * EPL, bv);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(bv[e], cpart[e], acc);
+        acc = group_sum<8>(acc);
+        const float t = __shfl(acc, (lane & 7) * 8, 64);
+        if ((lane >> 3) == q) bc = t;
+      }
+      coef = lane <= w ? wt * bc : 0.f;
+      coef_lds[wave * 64 + lane] = coef;  // broadcast to the wave through LDS
+      __builtin_amdgcn_wave_barrier();
+    }
+    // S0 . C per state row
+    RowDot<ST, IT, SV> rd;
+    rd.load(Cs, c);
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) part[it] = rd.dot(sv[it]);
+  } else {
+    // ================= flush tile: stream the tile in chunks, fold, store
+    u32x4 ra[IC], rb[IC];
+#pragma unroll
+    for (int q = 0; q < IC; ++q) ra[q] = bload16_nt(trs, lane_off, q * NT * 16);
+    if constexpr (NCH > 1) {
+#pragma unroll
+      for (int q = 0; q < IC; ++q) rb[q] = bload16_nt(trs, lane_off, (IC + q) * NT * 16);
+    }
+    stage();
+    load_dt();
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    finish_dt();
+    const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
+    cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
+    const float wt = lane <= w ? dti * expf(Ah * rsuf) : 0.f;
+    RowDot<ST, IT, SV> rd;
+    rd.load(Cs, c);
+    float cv[SV];
+    rd.cvals(cv);
+    SrCtx sr{a.sr_seed, a.sr_offset, ((uint64_t)s * H + h) * (uint64_t)(P * N / 16)};
+    FoldCtx fc{w, wt, cumdecay, Bs, xs, c, prow, trs, tptr, lane_off, sr};
+    fold_from<ST, IT, P, N, NT, SV, IC, RPI, ITEMS, 0, SR>(ra, rb, part, cv, fc);
+  }
+
+  // ---- whole rows per lane; ring term, D*x, gate, store
+  using RR = RowReduce<ITEMS, LPR>;
+  RR::run(part, tid);
+  const bool writer = (c % RR::DUP) == 0;
+#pragma unroll
+  for (int j = 0; j < RR::NF; ++j) {
+    const int p = RR::item(j, tid) * RPI + prow;
+    float yv = part[j];
+    if (!f) {
+      // coef is 0 past w; row indexes are clamped to w
+      yv *= cumdecay;
+      const float* cw = coef_lds + wave * 64;
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        yv = fmaf(cw[i], LdsRead<IT>::one(xs, (i <= w ? i : w) * P + p), yv);
+      for (int i = 16; i <= w; ++i) yv = fmaf(cw[i], LdsRead<IT>::one(xs, i * P + p), yv);
+    }
+    yv = fmaf(Dh, LdsRead<IT>::one(xs, w * P + p), yv);
+    if (a.z) yv = silu_gate(yv, LdsRead<IT>::one(zs, p));
+    if (writer) Elt<OT>::store1(a.y, yoff + p, yv);
+  }
+}
+
+template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY, bool SR>
+static int launch_mamba2(const Mamba2Args& a, int batch, hipStream_t stream) {
+  using TS = TileShape<ST, P, N, REPLAY>;
+  const int L = REPLAY ? a.ring_len : 1;  // L <= 64: one dt per lane of a wave
+  const size_t lds = (size_t)Stage<IT, P, N>::chunks(L) * 16;
+  if (lds > kMaxLds) return RSSM_ESHAPE;  // ring rows must fit one workgroup's LDS
+  const long grid = (long)batch * a.nheads;
+  return launch_kernel(
+      reinterpret_cast<const void*>(&mamba2_decode_kernel<ST, IT, OT, P, N, REPLAY, SR>),
+      (unsigned)grid, TS::NT, lds, stream, a);
+}
+
+template <bool REPLAY, bool SR, typename ST, typename IT, typename OT>
+static int dispatch_shape(const Mamba2Args& a, const rssm_dims& d, hipStream_t s) {
+#define RSSM_SHAPE(PP, NN) \
+  if (d.headdim == PP && d.dstate == NN)    \
+    return launch_mamba2<ST, IT, OT, PP, NN, REPLAY, SR>(a, d.batch, s);
+  RSSM_SHAPE(64, 128)
+  RSSM_SHAPE(64, 16)
+  RSSM_SHAPE(64, 32)
+  RSSM_SHAPE(64, 64)
+  RSSM_SHAPE(64, 256)
+  RSSM_SHAPE(32, 16)
+  RSSM_SHAPE(32, 32)
+  RSSM_SHAPE(32, 64)
+  RSSM_SHAPE(32, 128)
+  RSSM_SHAPE(32, 256)
+  RSSM_SHAPE(128, 16)
+  RSSM_SHAPE(128, 32)
+  RSSM_SHAPE(128, 64)
+  RSSM_SHAPE(128, 128)
+  RSSM_SHAPE(128, 256)
+#undef RSSM_SHAPE
+  return RSSM_ESHAPE;
+}
+
+// Dispatch on the dtypes: all eight combinations with nearest rounding;
+// stochastic rounding exists for the bf16 state pool only.
+template <bool REPLAY, bool SR>
+static int dispatch_mamba2(const Mamba2Args& a, const rssm_dims& d, hipStream_t s) {
+  const int key = d.state_dtype * 4 + d.io_dtype * 2 + d.out_dtype;
+  if constexpr (SR) {
+    switch (key) {
+      case 4: return dispatch_shape<REPLAY, true, bf16, float, float>(a, d, s);
+      case 5: return dispatch_shape<REPLAY, true, bf16, float, bf16>(a, d, s);
+      case 6: return dispatch_shape<REPLAY, true, bf16, bf16, float>(a, d, s);
+      case 7: return dispatch_shape<REPLAY, true, bf16, bf16, bf16>(a, d, s);
+    }
+  } else {
+    switch (key) {
+      case 0: return dispatch_shape<REPLAY, false, float, float, float>(a, d, s);
+      case 1: return dispatch_shape<REPLAY, false, float, float, bf16>(a, d, s);
+      case 2: return dispatch_shape<REPLAY, false, float, bf16, float>(a, d, s);
+      case 3: return dispatch_shape<REPLAY, false, float, bf16, bf16>(a, d, s);
+      case 4: return dispatch_shape<REPLAY, false, bf16, float, float>(a, d, s);
+      case 5: return dispatch_shape<REPLAY, false, bf16, float, bf16>(a, d, s);
+      case 6: return dispatch_shape<REPLAY, false, bf16, bf16, float>(a, d, s);
+      case 7: return dispatch_shape<REPLAY, false, bf16, bf16, bf16>(a, d, s);
+    }
+  }
+  return RSSM_EDTYPE;
+}
+
+// Stochastic-rounding instances (mamba2_sr.hip).
+int dispatch_mamba2_sr(bool replay, const Mamba2Args& a, const rssm_dims& d, hipStream_t s);
+
+}  // namespace rssm

@@ -286,6 +286,63 @@ template <> struct LdsRead<bf16> {
   }
 };
 
+// Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): a counter-based generator.  Each of the ten
+// rounds multiplies counter words 0 and 2 by the two round multipliers,
+// permutes the words as the 4x64 variant prescribes (high halves xored with
+// the other words and the key), and advances the key by the two Weyl
+// constants.  c holds the counter on entry and the 256 random bits on exit.
+__device__ static inline void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t kM0 = 0xD2E7470EE14C6C93ull, kM1 = 0xCA5A826395121157ull;
+  constexpr uint64_t kW0 = 0x9E3779B97F4A7C15ull, kW1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(kM0, c[0]), lo0 = kM0 * c[0];
+    const uint64_t hi1 = __umul64hi(kM1, c[2]), lo1 = kM1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+    k0 += kW0;
+    k1 += kW1;
+  }
+}
+
+// fp32 -> bf16 by stochastic rounding with 16 random bits r: adding r below
+// the kept 16 bits of the pattern carries into them with probability
+// (dropped part) / 2^16, so the result rounds away from zero with exactly
+// that probability (exact values are kept).  Inf and NaN keep the nearest
+// (bit-preserving) conversion.
+__device__ static inline uint32_t bf16_bits_sr(float f, uint32_t r) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u)
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
+  return (u + (r & 0xffffu)) >> 16;
+}
+
+// Eight fp32 values -> one 16-byte bf16 vector, element j using bits
+// 16*(j%4) .. of word j/4 of (w0, w1).
+__device__ static inline u32x4 bf16_pack_sr(const float* f, uint64_t w0, uint64_t w1) {
+  u32x4 v;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint64_t w = k < 2 ? w0 : w1;
+    const uint32_t lo = bf16_bits_sr(f[2 * k], (uint32_t)(w >> (32 * (k & 1))));
+    const uint32_t hi = bf16_bits_sr(f[2 * k + 1], (uint32_t)(w >> (32 * (k & 1) + 16)));
+    v[k] = lo | (hi << 16);
+  }
+  return v;
+}
+
+// Value of a 64-bit register in the other lane of an adjacent pair
+// (lane ^ 1), by DPP quad permutation [1, 0, 3, 2].
+__device__ static inline uint64_t swap_lane_pair(uint64_t x) {
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)x, 0xB1, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(x >> 32), 0xB1, 0xF, 0xF, false);
+  return (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32);
+}
+
 // softplus(v) = log(1 + e^v): v itself above 20 (exact in fp32).  log1p(e)
 // is taken as log(u) * e / (u - 1) with u = 1 + e, which cancels the
 // rounding of u (u - 1 is exact; accurate to a few ulp with the hardware log

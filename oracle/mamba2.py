@@ -42,7 +42,7 @@ with bit 2 are skipped (y = NaN, cursors reset).
 
 import numpy as np
 
-from .numerics import silu_gate, softplus, store
+from .numerics import store_tiles_sr, silu_gate, softplus, store
 
 ST_BAD_WRITE_POS = 1
 ST_RING_OVERFLOW = 2
@@ -64,15 +64,36 @@ def dt_process(dt_raw, dt_bias, dt_softplus):
     return softplus(v) if dt_softplus else v
 
 
+def _write_state(state, slots, S, state_dtype, rounding, sr_seed, sr_offset, sr_slots=None):
+    """Write state tiles S [k, H, P, N] to pool slots; nearest rounding or,
+    for a bf16 pool, stochastic rounding with tile index slot * H + head
+    (``sr_slots`` names the slots whose random bits to use when this pool is
+    a compact copy of a larger one)."""
+    slots = np.asarray(slots).reshape(-1)
+    if rounding == "stochastic":
+        if state_dtype != "bf16":
+            raise ValueError("stochastic rounding applies to a bf16 state")
+        H = S.shape[1]
+        ts = slots if sr_slots is None else np.asarray(sr_slots).reshape(-1)
+        tiles = ts[:, None] * H + np.arange(H)[None, :]
+        state[slots] = store_tiles_sr(S, tiles, sr_seed, sr_offset)
+    elif rounding == "nearest":
+        state[slots] = store(S, state_dtype)
+    else:
+        raise ValueError(f"unknown rounding {rounding!r}")
+
+
 def ssu_standard_step(state, slot_idx, x, dt_raw, A, B, C, D=None, z=None,
-                      dt_bias=None, dt_softplus=True, state_dtype="f64"):
+                      dt_bias=None, dt_softplus=True, state_dtype="f64",
+                      rounding="nearest", sr_seed=0, sr_offset=0, sr_slots=None):
     """One step of the standard (read + write) selective state update.
 
     For each row b (slot s = slot_idx[b]) and head h:
         dt = softplus(dt_raw + dt_bias)
         S  = exp(dt * A[h]) * S + dt * outer(x[b, h], B[b, g(h)])
         y  = S @ C[b, g(h)] + D[h] * x[b, h];   y *= z * sigmoid(z)
-    and S is written back to the pool in ``state_dtype``.
+    and S is written back to the pool in ``state_dtype`` (bf16 by nearest or
+    stochastic rounding, see ``numerics.store_tiles_sr``).
     ``state`` is modified in place; returns y as float64 [batch, H, P].
     """
     x = np.asarray(x, np.float64)
@@ -93,7 +114,7 @@ def ssu_standard_step(state, slot_idx, x, dt_raw, A, B, C, D=None, z=None,
         y = y + np.asarray(D, np.float64)[None, :, None] * x
     if z is not None:
         y = silu_gate(y, z)
-    state[slot_idx] = store(S, state_dtype)
+    _write_state(state, slot_idx, S, state_dtype, rounding, sr_seed, sr_offset, sr_slots)
     return y
 
 
@@ -117,7 +138,8 @@ def ring_reset(write_pos, is_flush, rows, L):
 
 def replay_step(state, x_ring, dt_ring, B_ring, slot_idx, write_pos, is_flush,
                 x, dt_raw, A, B, C, D=None, z=None, dt_bias=None,
-                dt_softplus=True, state_dtype="f64"):
+                dt_softplus=True, state_dtype="f64", rounding="nearest", sr_seed=0,
+                sr_offset=0, sr_slots=None):
     """One ReplaySSM output-only decode step over a batch.
 
     ``state`` (the checkpoint pool S0), ``x_ring`` [slots, H, L, P],
@@ -185,7 +207,8 @@ def replay_step(state, x_ring, dt_ring, B_ring, slot_idx, write_pos, is_flush,
             S_new = (cumdecay[:, None, None] * S0
                      + np.einsum("hi,hip,hin->hpn", wt, xs, Bs))
             yb = np.matmul(S_new, Cb[:, :, None])[..., 0]
-            state[s] = store(S_new, state_dtype)
+            _write_state(state, [s], S_new[None], state_dtype, rounding, sr_seed, sr_offset,
+                         None if sr_slots is None else [sr_slots[b]])
             nwp[b] = 0
         else:
             u = np.matmul(S0, Cb[:, :, None])[..., 0]   # [H, P]

@@ -48,8 +48,8 @@ class Tol:
     the fp32 bound ('rel'), or the larger of the two ('abs').
     """
 
-    def __init__(self, kind, tol, bf16_out=False):
-        self.kind, self.tol, self.bf16_out = kind, tol, bf16_out
+    def __init__(self, kind, tol, bf16_out=False, ulps=1):
+        self.kind, self.tol, self.bf16_out, self.ulps = kind, tol, bf16_out, ulps
 
     def err(self, got, ref):
         got = np.asarray(got, np.float64)
@@ -64,7 +64,7 @@ class Tol:
                 return float((d / bound).max() * self.tol)
             return float(d.max() / scale)
         if self.bf16_out:
-            return float((d / np.maximum(self.tol, bf16_ulp(ref))).max() * self.tol)
+            return float((d / np.maximum(self.tol, self.ulps * bf16_ulp(ref))).max() * self.tol)
         return float(d.max())
 
     def check(self, what, got, ref):
@@ -78,9 +78,19 @@ def _np(t):
     return t.detach().double().cpu().numpy()
 
 
+SR_SEED = 0x5EED5EED
+
+
 def run_mamba2(wl, sample, y_dtype=torch.float32, steps=None, tol_state=None,
-               tol_y=None, standard=True, check_every=1, dev="cuda:0"):
-    """Run a Mamba2 workload; returns a dict of worst errors seen."""
+               tol_y=None, standard=True, check_every=1, dev="cuda:0", rounding="nearest"):
+    """Run a Mamba2 workload; returns a dict of worst errors seen.
+
+    rounding="stochastic" (bf16 pools): every state store on both sides uses
+    the same Philox bits (key (SR_SEED, call counter)); values that land
+    between the two sides' fp32 results may round apart, so stored states
+    are compared with a two-ulp allowance, and the final replay-vs-recurrence
+    comparison is skipped (per-step stochastic rounding of the recurrence is
+    a random walk that the once-per-ring replay does not take)."""
     t0 = time.time()
     dev = torch.device(dev)
     gen = Mamba2Inputs(wl)
@@ -95,6 +105,10 @@ def run_mamba2(wl, sample, y_dtype=torch.float32, steps=None, tol_state=None,
         tol_y = Tol("rel", 2e-5, bf16_y) if fp32_path else Tol("abs", 1e-2, bf16_y)
     if tol_state is None:
         tol_state = Tol("rel", 2e-5) if fp32_path else Tol("abs", 1e-2)
+        if rounding == "stochastic":
+            tol_state = Tol("abs", 1e-2, True, ulps=2)
+    sr_on = rounding == "stochastic"
+    calls = [0]
     sample = sorted(set(int(r) for r in sample))
     k = len(sample)
 
@@ -135,29 +149,32 @@ def run_mamba2(wl, sample, y_dtype=torch.float32, steps=None, tol_state=None,
         gi = {n: v.to(dev) for n, v in inp.items()}
         flushing = c_fl.astype(bool).copy()
         w_before = c_wp.copy()
+        calls[0] += 1
+        sr_g = dict(rounding=rounding, sr_seed=SR_SEED, sr_offset=calls[0]) if sr_on else {}
+        sr_o = dict(sr_g, sr_slots=slots_np[sample]) if sr_on else {}
         y = R.replayssm_decode(st_r, xr, dr, br, sl, wp, fl, gi["x"], gi["dt"], gp["A"],
                                gi["B"], gi["C"], D=gp["D"], z=gi["z"],
                                dt_bias=gp["dt_bias"], next_write_pos=nwp,
-                               next_is_flush=nfl, status=status, out_dtype=y_dtype)
+                               next_is_flush=nfl, status=status, out_dtype=y_dtype, **sr_g)
         ys = None
         if standard:
             ys = R.ssu_standard_decode(st_s, sl, gi["x"], gi["dt"], gp["A"], gi["B"],
                                        gi["C"], D=gp["D"], z=gi["z"],
                                        dt_bias=gp["dt_bias"], status=status,
-                                       out_dtype=y_dtype)
+                                       out_dtype=y_dtype, **sr_g)
         wp, nwp = nwp, wp
         fl, nfl = nfl, fl
         ni = {n: v[samp_t].double().numpy() for n, v in inp.items()}
         y_ref, o_wp, o_fl, ost = OM.replay_step(
             o_pool, o_xr, o_dr, o_br, o_sl, o_wp, o_fl, ni["x"], ni["dt"], pn["A"],
             ni["B"], ni["C"], D=pn["D"], z=ni["z"], dt_bias=pn["dt_bias"],
-            state_dtype=sdt)
+            state_dtype=sdt, **sr_o)
         assert ost == 0
         # the recurrence always advances: it is also the reference for the
         # state the GPU's checkpoint + ring represent at the end
         ys_ref = OM.ssu_standard_step(o_rec, o_sl, ni["x"], ni["dt"], pn["A"], ni["B"],
                                       ni["C"], D=pn["D"], z=ni["z"],
-                                      dt_bias=pn["dt_bias"], state_dtype=sdt)
+                                      dt_bias=pn["dt_bias"], state_dtype=sdt, **sr_o)
         c_wp, c_fl = OM.cursor_advance(c_wp, c_fl, L)
         if not compare:
             return
@@ -218,6 +235,10 @@ def run_mamba2(wl, sample, y_dtype=torch.float32, steps=None, tol_state=None,
     # recurrence; and the standard update's state
     for j, r in enumerate(sample):
         s = int(slots_np[r])
+        if sr_on:
+            if standard:
+                tol_state.check(f"{wl.name} row {r} standard state", _np(st_s[s]), o_rec[j])
+            continue
         logical = OM.replay_logical_state(
             _np(st_r[s])[None], _np(xr[s])[None], _np(dr[s])[None], _np(br[s])[None],
             0, int(c_wp[r]), pn["A"])

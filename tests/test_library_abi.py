@@ -36,7 +36,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for fn in sorted(_declared()):
         assert hasattr(lib, fn), f"{fn} is declared but not exported"
     assert set(R.EXPORTS) <= _declared()
-    assert lib.replayssm_abi_version() == 100
+    assert lib.replayssm_abi_version() == 101
     assert lib.replayssm_strerror(-4).decode().startswith("shape")
 
 
@@ -70,6 +70,9 @@ def test_host_validation_rejects_bad_arguments_without_a_gpu():
     assert call(x=V(0x1004)) == -1                  # misaligned vector operand
     assert call(y=None) == -1                       # required pointer
     assert call(dims=dict(batch=0)) == 0            # empty batch: nothing to do
+    assert call(dims=dict(rounding=2)) == -1        # unknown rounding mode
+    assert call(dims=dict(rounding=1)) == -2        # stochastic rounding of an fp32 state
+    assert call(dims=dict(rounding=1, state_dtype=1, batch=0)) == 0
     gd = R.GdnDims(2, 1, 2, 128, 128, 4, 4, 1, 1, 1, 0.0)
     assert lib.gdn_standard_decode(ctypes.byref(gd), *([V(0x1000)] * 8), None, None) == -2
     d = R.Dims(**good)
