@@ -11,9 +11,11 @@ value = batch * steps / seconds (state-updates/s: one row advanced one step
 through one layer).
 
 Also measured in the same run (separate timed regions): the standard
-read+write update (ssu_standard_decode) on the same workload, and the GDN
-replay/standard decode at batch 256 (16 key / 32 value heads, K = V = 128,
-L = 16, bf16 q/k/v, fp32 state); and the float64 CPU oracle on a bounded
+read+write update (ssu_standard_decode) on the same workload; both again
+with stochastic rounding of the bf16 write-back; one tensor-parallel rank's
+share of the layer (10 of 80 heads); the GDN replay/standard decode at
+batch 256 (16 key / 32 value heads, K = V = 128, L = 16, bf16 q/k/v, fp32
+state); the host metadata builder; and the float64 CPU oracle on a bounded
 sample (``cpu_baseline``).
 
 Roofline: algorithmic bytes per launch (checkpoint reads, ring reads of the
@@ -29,6 +31,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 4]
 """
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -103,21 +106,23 @@ class Mamba2Layers:
         for l in range(self.nl):
             assert np.array_equal(self.wp[l].cpu().numpy(), self.w0), "warm-up cursors"
 
-    def replay(self, l, inp):
+    def replay(self, l, inp, sr=None):
         import linear_recurrence_amd as R
+        kw = {} if sr is None else dict(rounding="stochastic", sr_seed=17, sr_offset=sr)
         R.replayssm_decode(self.state[l], self.xr[l], self.dr[l], self.br[l], self.slots,
                            self.wp[l], self.fl[l], inp["x"], inp["dt"], self.prm["A"],
                            inp["B"], inp["C"], D=self.prm["D"], z=inp["z"],
                            dt_bias=self.prm["dt_bias"], y=self.y,
-                           next_write_pos=self.nwp[l], next_is_flush=self.nfl[l])
+                           next_write_pos=self.nwp[l], next_is_flush=self.nfl[l], **kw)
         self.wp[l], self.nwp[l] = self.nwp[l], self.wp[l]
         self.fl[l], self.nfl[l] = self.nfl[l], self.fl[l]
 
-    def standard(self, l, inp):
+    def standard(self, l, inp, sr=None):
         import linear_recurrence_amd as R
+        kw = {} if sr is None else dict(rounding="stochastic", sr_seed=17, sr_offset=sr)
         R.ssu_standard_decode(self.state[l], self.slots, inp["x"], inp["dt"], self.prm["A"],
                               inp["B"], inp["C"], D=self.prm["D"], z=inp["z"],
-                              dt_bias=self.prm["dt_bias"], y=self.y)
+                              dt_bias=self.prm["dt_bias"], y=self.y, **kw)
 
     def replay_bytes(self, step_in_layer):
         """Algorithmic bytes of one replay launch, from every row's cursor."""
@@ -148,35 +153,40 @@ def time_region(fn, steps, warmup):
     return e0.elapsed_time(e1) / 1e3  # seconds
 
 
-def bench_mamba2(wl, layers, steps, warmup, y_dtype, dev):
+def bench_mamba2(wl, layers, steps, warmup, y_dtype, dev, sr=False):
+    """Replay and standard timed regions; with sr, also both with stochastic
+    rounding of the bf16 write-back (a fresh Philox offset every call)."""
     M = Mamba2Layers(wl, layers, dev, y_dtype)
     M.warm_rings()
     # replay: step i uses layer i % layers; bytes are accounted per launch
     # from the cursors that layer has at that step
     step_of = [0] * layers
 
-    def rep(i):
+    def rep(i, sr_on=False):
         l = i % layers
-        M.replay(l, M.inputs[i % 8])
+        M.replay(l, M.inputs[i % 8], sr=i if sr_on else None)
         step_of[l] += 1
 
-    for i in range(warmup):
-        rep(i)
-    torch.cuda.synchronize()
-    local = list(step_of)
-    total_bytes = 0.0
-    for i in range(steps):
-        l = (warmup + i) % layers
-        total_bytes += M.replay_bytes(local[l])
-        local[l] += 1
-    t_rep = time_region(lambda i: rep(warmup + i), steps, 0)
-    for l in range(layers):
-        got = M.wp[l].cpu().numpy()
-        assert np.array_equal(got, (M.w0 + step_of[l]) % wl.ring_len), "cursor drift"
-    rep_bytes = total_bytes / steps
+    def replay_region(first, sr_on):
+        for i in range(warmup):
+            rep(first + i, sr_on)
+        torch.cuda.synchronize()
+        local = list(step_of)
+        total = 0.0
+        for i in range(steps):
+            l = (first + warmup + i) % layers
+            total += M.replay_bytes(local[l])
+            local[l] += 1
+        t = time_region(lambda i: rep(first + warmup + i, sr_on), steps, 0)
+        for l in range(layers):
+            got = M.wp[l].cpu().numpy()
+            assert np.array_equal(got, (M.w0 + step_of[l]) % wl.ring_len), "cursor drift"
+        return t, total / steps
 
-    def std(i):
-        M.standard(i % layers, M.inputs[i % 8])
+    t_rep, rep_bytes = replay_region(0, False)
+
+    def std(i, sr_on=False):
+        M.standard(i % layers, M.inputs[i % 8], sr=i if sr_on else None)
 
     t_std = time_region(std, steps, warmup)
     std_bytes = M.standard_bytes()
@@ -189,6 +199,15 @@ def bench_mamba2(wl, layers, steps, warmup, y_dtype, dev):
         "replay_GBps": rep_bytes * steps / t_rep / 1e9,
         "standard_GBps": std_bytes * steps / t_std / 1e9,
     }
+    if sr:
+        t_rsr, rsr_bytes = replay_region(warmup + steps, True)
+        t_ssr = time_region(lambda i: std(i, True), steps, warmup)
+        res["stochastic_rounding"] = {
+            "replay_updates_per_s": nb * steps / t_rsr,
+            "replay_GBps": rsr_bytes * steps / t_rsr / 1e9,
+            "standard_updates_per_s": nb * steps / t_ssr,
+            "standard_GBps": std_bytes * steps / t_ssr / 1e9,
+        }
     del M
     torch.cuda.empty_cache()
     return res
@@ -297,6 +316,22 @@ def cpu_baseline(wl, rows, steps):
                       f"steps ({L} desync warm-up steps first), one thread, {dt:.1f} s"}
 
 
+def metadata_rate(rows, L, calls=2000):
+    """Host metadata builder: rows per second on one core (decode bases and
+    positions of a batch, align mode with 16-token blocks)."""
+    import linear_recurrence_amd as R
+    rng = np.random.default_rng(0)
+    base = rng.integers(0, 4096, rows).astype(np.int64)
+    pos = base + rng.integers(0, 8, rows).astype(np.int64)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        R.build_metadata(pos, base, L, align_block=16)
+        pos += 1
+    dt = time.perf_counter() - t0
+    return {"rows_per_s": rows * calls / dt, "rows": rows, "calls": calls,
+            "note": "host C++ through the Python binding, one core"}
+
+
 def measured_traffic(path):
     """HBM bytes per replay launch from the committed counter summary, or
     None when there is none or the kernel sources changed since it was taken."""
@@ -342,6 +377,10 @@ def main():
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
                     help="per-launch HBM bytes measured with rocprofv3 counters")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-sr", action="store_true",
+                    help="skip the stochastic-rounding measurement")
+    ap.add_argument("--no-tp", action="store_true",
+                    help="skip the one-rank tensor-parallel share (10 heads)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -364,9 +403,24 @@ def main():
     y_dtype = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
     print(f"[bench] {wl.name}: layers={args.layers} steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
-    m = bench_mamba2(wl, args.layers, args.steps, args.warmup, y_dtype, dev)
+    m = bench_mamba2(wl, args.layers, args.steps, args.warmup, y_dtype, dev, sr=not args.no_sr)
     print(f"[bench] mamba2 done: {m['replay_GBps']:.0f} GB/s replay, "
           f"{m['standard_GBps']:.0f} GB/s standard", file=sys.stderr, flush=True)
+    tp = None
+    if not args.no_tp:
+        # one tensor-parallel rank's share of the same layer: 80 / 8 = 10 heads,
+        # 16 rotated layers so the working set stays far above the last-level cache
+        wl_tp = dataclasses.replace(wl, name="mamba2_b512_h10_L16_bf16state_tp8share",
+                                    nheads=10)
+        t = bench_mamba2(wl_tp, 16, args.steps, args.warmup, y_dtype, dev)
+        tp = {"workload": wl_tp.name, "nheads": 10, "layers_rotated": 16,
+              "replay_updates_per_s": t["replay_updates_per_s"],
+              "replay_GBps": t["replay_GBps"], "replay_frac": t["replay_GBps"] / PEAK_HBM_GBPS,
+              "standard_updates_per_s": t["standard_updates_per_s"],
+              "standard_GBps": t["standard_GBps"],
+              "speedup": t["replay_updates_per_s"] / t["standard_updates_per_s"]}
+        print(f"[bench] tp8 share done: {t['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
+              flush=True)
     gdn = None
     if not args.no_gdn:
         gdn = bench_gdn(GDN, args.layers, args.steps, args.warmup, dev)
@@ -421,6 +475,9 @@ def main():
         },
         "speedup_vs_standard": m["replay_updates_per_s"] / m["standard_updates_per_s"],
         "gdn": gdn,
+        "stochastic_rounding": m.get("stochastic_rounding"),
+        "tp8_share": tp,
+        "metadata_builder": metadata_rate(wl.batch, wl.ring_len),
     }
     print(json.dumps(line), flush=True)
 

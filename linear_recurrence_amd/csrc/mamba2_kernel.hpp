@@ -63,16 +63,17 @@ struct Mamba2Args {
   uint64_t sr_offset;
 };
 
-// Tile geometry.  The replay kernel streams 16 state vectors per lane where
-// the tile allows it (its per-tile staging is amortised over more bytes);
-// the standard update, which also writes every tile, runs 4 per lane (more
-// waves in flight).
-template <typename ST, int P, int N, bool REPLAY>
+// Tile geometry: PER target state vectors per lane.  The replay kernel
+// streams 16 per lane where the tile allows it (its per-tile staging is
+// amortised over more bytes) and 4 when the grid is too small to fill the
+// GPU that way; the standard update, which also writes every tile, runs 4
+// per lane (more waves in flight).
+template <typename ST, int P, int N, int PER_>
 struct TileShape {
   static constexpr int SV = Elt<ST>::kPer16;  // state elements per vector
   static constexpr int LPR = N / SV;          // lanes per state row
   static constexpr int NVEC = P * N / SV;     // vectors per tile
-  static constexpr int PER = REPLAY ? 16 : 4; // target vectors per lane
+  static constexpr int PER = PER_;            // target vectors per lane
   static constexpr int NT0 = NVEC / PER;
   static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 512 ? 512 : NT0);  // threads
   static constexpr int ITEMS = NVEC / NT;     // vectors per lane
@@ -287,10 +288,10 @@ __device__ __forceinline__ void fold_from(u32x4 (&ra)[IC], u32x4 (&rb)[IC], floa
   }
 }
 
-template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY, bool SR>
-__global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
+template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY, bool SR, int PER>
+__global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
     mamba2_decode_kernel(const Mamba2Args a) {
-  using TS = TileShape<ST, P, N, REPLAY>;
+  using TS = TileShape<ST, P, N, PER>;
   using SG = Stage<IT, P, N>;
   constexpr int SV = TS::SV, LPR = TS::LPR, NT = TS::NT, ITEMS = TS::ITEMS, RPI = TS::RPI;
   constexpr int IC = TS::IC, NCH = TS::NCH;
@@ -528,23 +529,23 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, REPLAY>::NT))
   }
 }
 
-template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY, bool SR>
+template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY, bool SR, int PER>
 static int launch_mamba2(const Mamba2Args& a, int batch, hipStream_t stream) {
-  using TS = TileShape<ST, P, N, REPLAY>;
+  using TS = TileShape<ST, P, N, PER>;
   const int L = REPLAY ? a.ring_len : 1;  // L <= 64: one dt per lane of a wave
   const size_t lds = (size_t)Stage<IT, P, N>::chunks(L) * 16;
   if (lds > kMaxLds) return RSSM_ESHAPE;  // ring rows must fit one workgroup's LDS
   const long grid = (long)batch * a.nheads;
   return launch_kernel(
-      reinterpret_cast<const void*>(&mamba2_decode_kernel<ST, IT, OT, P, N, REPLAY, SR>),
+      reinterpret_cast<const void*>(&mamba2_decode_kernel<ST, IT, OT, P, N, REPLAY, SR, PER>),
       (unsigned)grid, TS::NT, lds, stream, a);
 }
 
-template <bool REPLAY, bool SR, typename ST, typename IT, typename OT>
+template <bool REPLAY, bool SR, int PER, typename ST, typename IT, typename OT>
 static int dispatch_shape(const Mamba2Args& a, const rssm_dims& d, hipStream_t s) {
 #define RSSM_SHAPE(PP, NN) \
   if (d.headdim == PP && d.dstate == NN)    \
-    return launch_mamba2<ST, IT, OT, PP, NN, REPLAY, SR>(a, d.batch, s);
+    return launch_mamba2<ST, IT, OT, PP, NN, REPLAY, SR, PER>(a, d.batch, s);
   RSSM_SHAPE(64, 128)
   RSSM_SHAPE(64, 16)
   RSSM_SHAPE(64, 32)
@@ -566,26 +567,26 @@ static int dispatch_shape(const Mamba2Args& a, const rssm_dims& d, hipStream_t s
 
 // Dispatch on the dtypes: all eight combinations with nearest rounding;
 // stochastic rounding exists for the bf16 state pool only.
-template <bool REPLAY, bool SR>
+template <bool REPLAY, bool SR, int PER>
 static int dispatch_mamba2(const Mamba2Args& a, const rssm_dims& d, hipStream_t s) {
   const int key = d.state_dtype * 4 + d.io_dtype * 2 + d.out_dtype;
   if constexpr (SR) {
     switch (key) {
-      case 4: return dispatch_shape<REPLAY, true, bf16, float, float>(a, d, s);
-      case 5: return dispatch_shape<REPLAY, true, bf16, float, bf16>(a, d, s);
-      case 6: return dispatch_shape<REPLAY, true, bf16, bf16, float>(a, d, s);
-      case 7: return dispatch_shape<REPLAY, true, bf16, bf16, bf16>(a, d, s);
+      case 4: return dispatch_shape<REPLAY, true, PER, bf16, float, float>(a, d, s);
+      case 5: return dispatch_shape<REPLAY, true, PER, bf16, float, bf16>(a, d, s);
+      case 6: return dispatch_shape<REPLAY, true, PER, bf16, bf16, float>(a, d, s);
+      case 7: return dispatch_shape<REPLAY, true, PER, bf16, bf16, bf16>(a, d, s);
     }
   } else {
     switch (key) {
-      case 0: return dispatch_shape<REPLAY, false, float, float, float>(a, d, s);
-      case 1: return dispatch_shape<REPLAY, false, float, float, bf16>(a, d, s);
-      case 2: return dispatch_shape<REPLAY, false, float, bf16, float>(a, d, s);
-      case 3: return dispatch_shape<REPLAY, false, float, bf16, bf16>(a, d, s);
-      case 4: return dispatch_shape<REPLAY, false, bf16, float, float>(a, d, s);
-      case 5: return dispatch_shape<REPLAY, false, bf16, float, bf16>(a, d, s);
-      case 6: return dispatch_shape<REPLAY, false, bf16, bf16, float>(a, d, s);
-      case 7: return dispatch_shape<REPLAY, false, bf16, bf16, bf16>(a, d, s);
+      case 0: return dispatch_shape<REPLAY, false, PER, float, float, float>(a, d, s);
+      case 1: return dispatch_shape<REPLAY, false, PER, float, float, bf16>(a, d, s);
+      case 2: return dispatch_shape<REPLAY, false, PER, float, bf16, float>(a, d, s);
+      case 3: return dispatch_shape<REPLAY, false, PER, float, bf16, bf16>(a, d, s);
+      case 4: return dispatch_shape<REPLAY, false, PER, bf16, float, float>(a, d, s);
+      case 5: return dispatch_shape<REPLAY, false, PER, bf16, float, bf16>(a, d, s);
+      case 6: return dispatch_shape<REPLAY, false, PER, bf16, bf16, float>(a, d, s);
+      case 7: return dispatch_shape<REPLAY, false, PER, bf16, bf16, bf16>(a, d, s);
     }
   }
   return RSSM_EDTYPE;
@@ -593,5 +594,8 @@ static int dispatch_mamba2(const Mamba2Args& a, const rssm_dims& d, hipStream_t 
 
 // Stochastic-rounding instances (mamba2_sr.hip).
 int dispatch_mamba2_sr(bool replay, const Mamba2Args& a, const rssm_dims& d, hipStream_t s);
+// Replay instances with 4 vectors per lane, for grids too small to fill the
+// GPU with 16 (mamba2_small.hip).
+int dispatch_mamba2_small(const Mamba2Args& a, const rssm_dims& d, hipStream_t s);
 
 }  // namespace rssm

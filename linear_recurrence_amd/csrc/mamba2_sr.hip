@@ -6,7 +6,7 @@
 namespace rssm {
 
 int dispatch_mamba2_sr(bool replay, const Mamba2Args& a, const rssm_dims& d, hipStream_t s) {
-  return replay ? dispatch_mamba2<true, true>(a, d, s) : dispatch_mamba2<false, true>(a, d, s);
+  return replay ? dispatch_mamba2<true, true, 16>(a, d, s) : dispatch_mamba2<false, true, 4>(a, d, s);
 }
 
 }  // namespace rssm

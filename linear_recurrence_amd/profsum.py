@@ -28,7 +28,8 @@ import sys
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = {
-    "mamba2_decode_kernel": ("mamba2_decode.hip", "rssm_device.hpp", "rssm_host.hpp"),
+    "mamba2_decode_kernel": ("mamba2_kernel.hpp", "mamba2_decode.hip", "rssm_device.hpp",
+                             "rssm_host.hpp"),
     "gdn_decode_kernel": ("gdn_decode.hip", "rssm_device.hpp", "rssm_host.hpp"),
 }
 
@@ -49,9 +50,11 @@ def _rows(path):
 
 
 def _is_replay(name):
-    # template argument REPLAY is the last one: "..., true>(" / "..., false>("
-    return name.rstrip().endswith("true>(rssm::Mamba2Args)") or \
-        name.rstrip().endswith("true>(rssm::GdnArgs)")
+    """The REPLAY template argument of a kernel name: the sixth of
+    mamba2_decode_kernel<ST, IT, OT, P, N, REPLAY, SR, PER>, the last of
+    gdn_decode_kernel<IT, OT, V, K, REPLAY>."""
+    args = [a.strip() for a in name[name.index("<") + 1:name.rindex(">(")].split(",")]
+    return (args[5] if "mamba2_decode_kernel" in name else args[-1]) == "true"
 
 
 def _dispatch_kib(path, kernel, replay, last):

@@ -62,6 +62,27 @@ def test_every_supported_tile_shape(P, N):
     run_mamba2(wl, sample=range(3))
 
 
+def _one_wave_grid(P, N, state_dt, H=16):
+    """Rows enough that the replay grid takes the one-wave-per-16-KB path
+    (at least 8192 waves of 16 state vectors per lane)."""
+    tile = P * N * (2 if state_dt == "bf16" else 4)
+    per_tile = max(1, tile // 16384)
+    return -(-8192 // (H * per_tile))
+
+
+@pytest.mark.parametrize("P", [32, 64, 128])
+@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
+def test_every_tile_shape_on_a_full_grid(P, N):
+    """The same shapes on grids large enough for 16 vectors per lane (the
+    small grids above run 4 per lane); alternating dtypes; sampled rows."""
+    state_dt, io_dt = (("bf16", "bf16") if (P // 32 + N // 16) % 2 else ("f32", "bf16"))
+    nb = _one_wave_grid(P, N, state_dt)
+    print(f"case: full grid P={P} N={N} batch={nb} state={state_dt}", flush=True)
+    wl = Mamba2Workload(f"grid_p{P}_n{N}", nb, 16, P, N, 2, 3, 4, nb, io_dt, state_dt,
+                        2200 + P + N, desync=True)
+    run_mamba2(wl, sample=[0, nb // 2, nb - 1], standard=False)
+
+
 def test_layer_2p7b_full_size():
     """64 rows, 80 heads, dstate 128, L=16, bf16 io, fp32 pool of 1024 slots,
     256 steps; every row's cursors checked, 8 rows against the oracle."""
