@@ -244,6 +244,53 @@ int replayssm_gdn_decode(const rssm_gdn_dims* dims, void* state, float* d_ring,
                          int32_t* status, hipStream_t stream);
 
 /*
+ * GDN speculative decoding from the ring (sglang #28695 "[GDN] Support
+ * ReplaySSM Ring Spec-Verify": Implementation items 2-4 - a per-slot ring of
+ * d, k, g plus the raw inputs v, k, beta; the verify rebuilds every draft's
+ * output from the frozen checkpoint and the ring; the commit advances the
+ * cursor and, on flush, replays the raw inputs in order through the
+ * recurrent update ("exact fold"); linear draft chains only; the ring holds
+ * at least twice the drafts).  Per slot the rings are those of
+ * replayssm_gdn_decode plus v_ring [num_slots, HV, L, V] (io_dtype [16B]) and
+ * beta_ring [num_slots, HV, L] float32.  1 <= n_draft (T) <= 8 and
+ * 2*T <= ring_len <= 64 (RSSM_ESHAPE otherwise).
+ *
+ * replayssm_gdn_spec_verify - for row b at cursor w (entries 0..w-1
+ * committed; w + T <= L, else RSSM_ST_RING_OVERFLOW and o = NaN for the
+ * row), draft t is ring entry p = w + t and is formed exactly like a decode
+ * step of replayssm_gdn_decode at position p (Gamma and gamma over entries
+ * 0..p, pred, d_p, o).  Writes o [batch, T, HV, V] (out_dtype) and ring
+ * entries w..w+T-1 (d, k, g, v, beta); the state and the cursor are not
+ * modified.  q, k [batch, T, HK, K] and v [batch, T, HV, V] io_dtype [16B];
+ * g, beta [batch, T, HV] float32.
+ */
+int replayssm_gdn_spec_verify(const rssm_gdn_dims* dims, int32_t n_draft,
+                              const void* state, float* d_ring, void* k_ring,
+                              float* g_ring, void* v_ring, float* beta_ring,
+                              const int32_t* slot_idx, const int32_t* write_pos,
+                              const void* q, const void* k, const void* v,
+                              const float* g, const float* beta, void* o,
+                              int32_t* status, hipStream_t stream);
+
+/*
+ * replayssm_gdn_spec_commit - keep accepted[b] (0..T) verified drafts:
+ * w' = write_pos[b] + accepted[b].  If w' + T > ring_len (the next verify
+ * would not fit) or force_flush[b] != 0 (force_flush may be NULL), the state
+ * is rebuilt by the recurrence over entries 0..w'-1 from their raw inputs,
+ *     S = g_i*S;  d = beta_i*(v_i - S@k_i);  S += outer(d, k_i),
+ * stored, and w' = 0.  Writes next_write_pos[b] = w' (must not alias
+ * write_pos) and flushed[b] (may be NULL).  accepted outside [0, T] sets
+ * RSSM_ST_RING_OVERFLOW and is clamped.
+ */
+int replayssm_gdn_spec_commit(const rssm_gdn_dims* dims, int32_t n_draft, void* state,
+                              const void* k_ring, const float* g_ring,
+                              const void* v_ring, const float* beta_ring,
+                              const int32_t* slot_idx, const int32_t* write_pos,
+                              const int32_t* accepted, const uint8_t* force_flush,
+                              int32_t* next_write_pos, uint8_t* flushed,
+                              int32_t* status, hipStream_t stream);
+
+/*
  * Host-side metadata (HOST pointers; plain CPU code, nothing is enqueued).
  *
  * replayssm_build_metadata - per-row cursors of one decode step from token

@@ -19,7 +19,8 @@ import torch  # loads the HIP runtime the library then binds to
 
 __all__ = [
     "ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
-    "gdn_standard_decode", "replayssm_gdn_decode", "build_metadata",
+    "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
+    "replayssm_gdn_spec_commit", "build_metadata",
     "check_copy_sources", "library_path", "load",
     "RssmError", "ST_BAD_WRITE_POS", "ST_RING_OVERFLOW", "ST_BAD_SLOT",
     "ST_BAD_ROW", "EXPORTS",
@@ -30,7 +31,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libreplayss
 F32, BF16 = 0, 1
 ST_BAD_WRITE_POS, ST_RING_OVERFLOW, ST_BAD_SLOT, ST_BAD_ROW = 1, 2, 4, 8
 EXPORTS = ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
-           "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_build_metadata",
+           "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
+           "replayssm_gdn_spec_commit", "replayssm_build_metadata",
            "replayssm_check_copy_sources", "replayssm_strerror", "replayssm_abi_version")
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -82,8 +84,11 @@ def load():
     lib.replayssm_ring_reset.argtypes = [ctypes.POINTER(Dims), P, P, P, I, P, P]
     lib.gdn_standard_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 10
     lib.replayssm_gdn_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 17
+    lib.replayssm_gdn_spec_verify.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 16
+    lib.replayssm_gdn_spec_commit.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 13
     for fn in ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
-               "gdn_standard_decode", "replayssm_gdn_decode"):
+               "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
+               "replayssm_gdn_spec_commit"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.replayssm_build_metadata.argtypes = [I, I, I, P, P, P, P, P]
     lib.replayssm_build_metadata.restype = ctypes.c_int
@@ -361,3 +366,77 @@ def replayssm_gdn_decode(state, d_ring, k_ring, g_ring, slot_idx, write_pos,
         _ptr(o), _ptr(status), _stream(stream))
     _check("replayssm_gdn_decode", rc)
     return o
+
+
+def _spec_rings(state, d_ring, k_ring, g_ring, v_ring, beta_ring, io, dev):
+    ns, HV, V, K = state.shape
+    _need(k_ring, "k_ring", io, dev=dev)
+    HK, L = k_ring.shape[1], k_ring.shape[2]
+    _need(k_ring, "k_ring", io, (ns, HK, L, K))
+    if d_ring is not None:
+        _need(d_ring, "d_ring", torch.float32, (ns, HV, L, V), dev=dev)
+    _need(g_ring, "g_ring", torch.float32, (ns, HV, L), dev=dev)
+    _need(v_ring, "v_ring", io, (ns, HV, L, V), dev=dev)
+    _need(beta_ring, "beta_ring", torch.float32, (ns, HV, L), dev=dev)
+    return HK, L
+
+
+def replayssm_gdn_spec_verify(state, d_ring, k_ring, g_ring, v_ring, beta_ring, slot_idx,
+                              write_pos, q, k, v, g, beta, o=None, scale=None, status=None,
+                              out_dtype=None, stream=None):
+    """Verify T draft tokens per row from the checkpoint and the ring; returns o.
+
+    q, k [batch, T, HK, K]; v [batch, T, HV, V] (io dtype); g, beta
+    [batch, T, HV] float32; o [batch, T, HV, V].  Writes ring entries
+    w..w+T-1; leaves the state and the cursors alone.
+    """
+    dev = _need(state, "state", torch.float32).device
+    ns, HV, V, K = state.shape
+    _need(q, "q", (torch.float32, torch.bfloat16), dev=dev)
+    nb, T, HK = q.shape[0], q.shape[1], q.shape[2]
+    io = q.dtype
+    _need(q, "q", io, (nb, T, HK, K))
+    _need(k, "k", io, (nb, T, HK, K), dev=dev)
+    _need(v, "v", io, (nb, T, HV, V), dev=dev)
+    _need(g, "g", torch.float32, (nb, T, HV), dev=dev)
+    _need(beta, "beta", torch.float32, (nb, T, HV), dev=dev)
+    _, L = _spec_rings(state, d_ring, k_ring, g_ring, v_ring, beta_ring, io, dev)
+    _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
+    _need(write_pos, "write_pos", torch.int32, (nb,), dev=dev)
+    _opt(status, "status", torch.int32, (1,))
+    if o is None:
+        o = torch.empty((nb, T, HV, V), dtype=out_dtype or io, device=dev)
+    _need(o, "o", (torch.float32, torch.bfloat16), (nb, T, HV, V), dev=dev)
+    d = GdnDims(nb, HK, HV, K, V, L, ns, F32, _DT[io], _DT[o.dtype],
+                0.0 if scale is None else float(scale))
+    rc = load().replayssm_gdn_spec_verify(
+        ctypes.byref(d), ctypes.c_int32(T), _ptr(state), _ptr(d_ring), _ptr(k_ring),
+        _ptr(g_ring), _ptr(v_ring), _ptr(beta_ring), _ptr(slot_idx), _ptr(write_pos), _ptr(q),
+        _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o), _ptr(status), _stream(stream))
+    _check("replayssm_gdn_spec_verify", rc)
+    return o
+
+
+def replayssm_gdn_spec_commit(state, k_ring, g_ring, v_ring, beta_ring, slot_idx, write_pos,
+                              accepted, n_draft, next_write_pos, force_flush=None,
+                              flushed=None, status=None, stream=None):
+    """Keep the accepted drafts; rows whose next verify would not fit (or
+    forced) fold their ring into the state by the exact recurrence."""
+    dev = _need(state, "state", torch.float32).device
+    ns, HV, V, K = state.shape
+    io = k_ring.dtype
+    HK, L = _spec_rings(state, None, k_ring, g_ring, v_ring, beta_ring, io, dev)
+    nb = slot_idx.shape[0]
+    _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
+    _need(write_pos, "write_pos", torch.int32, (nb,), dev=dev)
+    _need(accepted, "accepted", torch.int32, (nb,), dev=dev)
+    _need(next_write_pos, "next_write_pos", torch.int32, (nb,), dev=dev)
+    _opt(force_flush, "force_flush", torch.uint8, (nb,), dev=dev)
+    _opt(flushed, "flushed", torch.uint8, (nb,), dev=dev)
+    _opt(status, "status", torch.int32, (1,))
+    d = GdnDims(nb, HK, HV, K, V, L, ns, F32, _DT[io], _DT[io], 0.0)
+    rc = load().replayssm_gdn_spec_commit(
+        ctypes.byref(d), ctypes.c_int32(n_draft), _ptr(state), _ptr(k_ring), _ptr(g_ring),
+        _ptr(v_ring), _ptr(beta_ring), _ptr(slot_idx), _ptr(write_pos), _ptr(accepted),
+        _ptr(force_flush), _ptr(next_write_pos), _ptr(flushed), _ptr(status), _stream(stream))
+    _check("replayssm_gdn_spec_commit", rc)

@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libreplayssm.so")
 SOURCES = ("mamba2_decode.hip", "mamba2_sr.hip", "mamba2_small.hip", "gdn_decode.hip",
-           "metadata.cpp")
+           "gdn_spec.hip", "metadata.cpp")
 CXX = os.environ.get("CXX", "g++")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -1,0 +1,551 @@
+// GDN speculative verify from the checkpoint + ring, and the commit with its
+// exact fold, for gfx950.
+//
+// Method: sglang #28695 "[GDN] Support ReplaySSM Ring Spec-Verify" -
+// Motivation (the recurrent verify keeps a full state snapshot per draft
+// token), Implementation items 2-4 (per-slot ring of d, k, g and of the raw
+// inputs v, k, beta; a verify kernel that rebuilds every draft's output from
+// the frozen checkpoint and the ring; an exact-fold kernel that replays the
+// raw inputs in order through the recurrent update on flush; the commit
+// advances the cursor instead of copying a snapshot; linear draft chains;
+// ring length at least twice the draft count) and the review notes (the
+// closed-form fold drifted on long outputs, the exact fold restored parity).
+// Formulas: see the contract in replayssm.h.
+//
+// Verify mapping: one workgroup per (row, value head) fp32 [V, K] tile, the
+// tile read once into registers; q, v of the T drafts, the k rows of the
+// committed entries and of the drafts, and the committed d rows staged in
+// LDS by direct-to-LDS loads.  Wave 0 forms, per draft t at ring position
+// p = w + t, the gate products (DPP suffix products over the lanes holding
+// g_0..g_p) and the weighted dots gamma_i*(k_i.k_p), gamma_i*(k_i.q_t);
+// every lane forms S0.k_p and S0.q_t for its state rows (2T butterfly row
+// reductions) and then walks the drafts in order, keeping the new d values
+// of its rows in registers.  The drafts' (d, k, g, v, beta) are written to
+// ring entries w..w+T-1; the state and the cursor are not touched.
+//
+// Commit mapping: one workgroup per (row, value head); rows that do not
+// flush only advance the cursor.  Flushing tiles hold the state in fp32
+// registers and apply the recurrence entry by entry (scale by g, row dots
+// with k by butterfly reduction, d shared through LDS, rank-1 update), then
+// store it.
+#include <math.h>
+
+#include "gdn_common.hpp"
+#include "rssm_device.hpp"
+#include "rssm_host.hpp"
+
+namespace rssm {
+
+constexpr int kMaxDraft = 8;
+
+struct SpecArgs {
+  float* state;
+  float* d_ring;
+  void* k_ring;
+  float* g_ring;
+  void* v_ring;
+  float* beta_ring;
+  const int32_t* slot_idx;
+  const int32_t* write_pos;
+  const int32_t* accepted;
+  const uint8_t* force_flush;
+  int32_t* next_write_pos;
+  uint8_t* flushed;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* g;
+  const float* beta;
+  void* o;
+  int32_t* status;
+  int32_t k_heads;
+  int32_t v_heads;
+  int32_t vpk;
+  int32_t ring_len;
+  int32_t num_slots;
+  int32_t n_draft;
+  float scale;
+};
+
+// Verify LDS, 16-byte chunks: [q rows 0..T-1 | v rows 0..T-1 |
+// k rows 0..L-1 (multiple of 8) | d rows 0..L-1 (fp32)]
+template <typename IT, int V, int K>
+struct VerifyStage {
+  static constexpr int IV = Elt<IT>::kPer16;
+  static constexpr int QV = K / IV;
+  static constexpr int VV = V / IV;
+  static constexpr int DV = V / 4;
+  static constexpr int oV(int T) { return T * QV; }
+  static constexpr int oK(int T) { return T * (QV + VV); }
+  static constexpr int oD(int T, int L) { return oK(T) + ((L + 7) & ~7) * QV; }
+  static constexpr int chunks(int T, int L) { return oD(T, L) + L * DV; }
+};
+
+// 16-byte chunks [c0, c0+n) of LDS from global memory, one wave-wide
+// direct-to-LDS load per 64 chunks; chunk u comes from src + 16*u.
+__device__ static inline void dma_rows(char* lds, int c0, int n, const char* src, int wave,
+                                       int lane, int nt) {
+  for (int j = wave * 64; j < n; j += nt) {
+    const int u = j + lane;
+    if (u < n) dma16(src + (long)u * 16, lds + (long)(c0 + j) * 16);
+  }
+}
+
+template <typename IT, typename OT, int V, int K>
+__global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_kernel(const SpecArgs a) {
+  using GS = GdnShape<V, K, true>;
+  using SG = VerifyStage<IT, V, K>;
+  constexpr int SV = GS::SV, LPR = GS::LPR, NT = GS::NT, ITEMS = GS::ITEMS, RPI = GS::RPI;
+  constexpr int QV = SG::QV, VV = SG::VV, DV = SG::DV;
+  constexpr long kIo = sizeof(IT);
+  using RR = RowReduce<ITEMS, LPR>;
+
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  __shared__ float cK[kMaxDraft][64];  // gamma_{i,t} * (k_i . k_{w+t}), i < w+t
+  __shared__ float cQ[kMaxDraft][64];  // gamma_{i,t} * (k_i . q_t),     i <= w+t
+  __shared__ float gamS[kMaxDraft];    // Gamma_t = prod_{j <= w+t} g_j
+
+  const int HV = a.v_heads, HK = a.k_heads, T = a.n_draft, L = a.ring_len;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int b = tile / HV;
+  const int hv = tile - b * HV;
+  const int hk = hv / a.vpk;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int s = a.slot_idx[b];
+  const int w = a.write_pos[b];
+  int st = 0;
+  if (s < 0 || s >= a.num_slots) st |= RSSM_ST_BAD_SLOT;
+  if (w < 0 || w + T > L) st |= RSSM_ST_RING_OVERFLOW;
+  if (st) {
+    if (hv == 0 && tid == 0 && a.status) atomicOr(a.status, st);
+    for (int e = tid; e < T * V; e += NT) {
+      const int t = e / V;
+      Elt<OT>::store1(a.o, ((long)(b * T + t) * HV + hv) * V + (e - t * V), __builtin_nanf(""));
+    }
+    return;
+  }
+
+  // ---- 1. every global read: the tile, then the staged rows, then gates
+  char* const tptr = (char*)a.state + ((long)s * HV + hv) * (long)V * K * 4;
+  const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(V * K * 4));
+  const uint32_t lane_off = tid * 16;
+  u32x4 sv[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
+
+  const long kring0 = ((long)s * HK + hk) * (long)L * K;
+  const long dring0 = ((long)s * HV + hv) * (long)L * V;
+  const long gring0 = ((long)s * HV + hv) * L;
+  const int oV = SG::oV(T), oK = SG::oK(T), oD = SG::oD(T, L);
+  for (int t = 0; t < T; ++t) {
+    const long qk = ((long)(b * T + t) * HK + hk) * K;
+    dma_rows(lds, t * QV, QV, (const char*)a.q + qk * kIo, wave, lane, NT);
+    dma_rows(lds, oK + (w + t) * QV, QV, (const char*)a.k + qk * kIo, wave, lane, NT);
+    dma_rows(lds, oV + t * VV, VV, (const char*)a.v + ((long)(b * T + t) * HV + hv) * V * kIo,
+             wave, lane, NT);
+  }
+  if (w > 0) {
+    dma_rows(lds, oK, w * QV, (const char*)a.k_ring + kring0 * kIo, wave, lane, NT);
+    dma_rows(lds, oD, w * DV, (const char*)(a.d_ring + dring0), wave, lane, NT);
+  }
+  // gate of ring entry `lane` (committed entries, then the drafts); 1 past them
+  float gl = 1.f;
+  if (lane < w) gl = a.g_ring[gring0 + lane];
+  else if (lane < w + T) gl = a.g[(long)(b * T + (lane - w)) * HV + hv];
+  const float bl = lane < T ? a.beta[(long)(b * T + lane) * HV + hv] : 0.f;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  const char* Qs = lds;
+  const char* Vs = lds + (long)oV * 16;
+  const char* Ks = lds + (long)oK * 16;
+  float* Ds = reinterpret_cast<float*>(lds + (long)oD * 16);
+
+  // ---- 2. wave 0: gate products and weighted dots of every draft
+  if (wave == 0) {
+    constexpr int EPL = K / 16;
+    const int q16 = lane & 15;
+    for (int t = 0; t < T; ++t) {
+      const int p = w + t;
+      const float gt = lane <= p ? gl : 1.f;
+      const float gam = L <= 16 ? row16_suffix_product_exclusive(gt)
+                                : wave_suffix_product_exclusive(gt, lane);
+      if (lane == 0) gamS[t] = gt * gam;
+      SegDot<IT, EPL> kp, qt;
+      kp.load(Ks + (long)p * QV * 16, q16 * EPL);
+      qt.load(Qs + (long)t * QV * 16, q16 * EPL);
+      float kk = 0.f, kq = 0.f;
+      for (int pass = 0; pass * 4 <= p; ++pass) {
+        const int i = pass * 4 + (lane >> 4);  // rows past p: unused values
+        SegDot<IT, EPL> ki;
+        ki.load(Ks + (long)i * QV * 16, q16 * EPL);
+        float a1 = group_sum<16>(ki.dot(kp));
+        float a2 = group_sum<16>(ki.dot(qt));
+        a1 = __shfl(a1, (lane & 3) * 16, 64);
+        a2 = __shfl(a2, (lane & 3) * 16, 64);
+        if ((lane >> 2) == pass) {
+          kk = a1;
+          kq = a2;
+        }
+      }
+      cK[t][lane] = lane < p ? gam * kk : 0.f;
+      cQ[t][lane] = lane <= p ? gam * kq : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // ---- 3. S0 . k_{w+t} and S0 . q_t for this lane's state rows
+  const int c = tid % LPR;
+  const int prow = tid / LPR;
+  float pk[kMaxDraft][RR::NF], pq[kMaxDraft][RR::NF];
+#pragma unroll
+  for (int t = 0; t < kMaxDraft; ++t) {
+    if (t < T) {
+      float kseg[SV], qseg[SV];
+      LdsRead<IT>::template seg<SV>(Ks + (long)(w + t) * QV * 16, c * SV, kseg);
+      LdsRead<IT>::template seg<SV>(Qs + (long)t * QV * 16, c * SV, qseg);
+      float a1[ITEMS], a2[ITEMS];
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it) {
+        float sf[SV];
+        Elt<float>::unpack(sv[it], sf);
+        float x1 = 0.f, x2 = 0.f;
+#pragma unroll
+        for (int j = 0; j < SV; ++j) {
+          x1 = fmaf(sf[j], kseg[j], x1);
+          x2 = fmaf(sf[j], qseg[j], x2);
+        }
+        a1[it] = x1;
+        a2[it] = x2;
+      }
+      RR::run(a1, tid);
+      RR::run(a2, tid);
+#pragma unroll
+      for (int j = 0; j < RR::NF; ++j) {
+        pk[t][j] = a1[j];
+        pq[t][j] = a2[j];
+      }
+    }
+  }
+
+  // ---- 4. per state row, the drafts in order
+  const bool writer = (c % RR::DUP) == 0;
+#pragma unroll
+  for (int j = 0; j < RR::NF; ++j) {
+    const int vr = RR::item(j, tid) * RPI + prow;
+    float hist_k[kMaxDraft], hist_q[kMaxDraft];  // committed-entry terms per draft
+#pragma unroll
+    for (int t = 0; t < kMaxDraft; ++t) hist_k[t] = hist_q[t] = 0.f;
+    for (int i = 0; i < w; ++i) {
+      const float di = Ds[i * V + vr];
+#pragma unroll
+      for (int t = 0; t < kMaxDraft; ++t) {
+        if (t < T) {
+          hist_k[t] = fmaf(cK[t][i], di, hist_k[t]);
+          hist_q[t] = fmaf(cQ[t][i], di, hist_q[t]);
+        }
+      }
+    }
+    float dn[kMaxDraft];
+#pragma unroll
+    for (int t = 0; t < kMaxDraft; ++t) {
+      dn[t] = 0.f;
+      if (t < T) {
+        const float G = gamS[t];
+        float pred = fmaf(G, pk[t][j], hist_k[t]);
+#pragma unroll
+        for (int u = 0; u < t; ++u) pred = fmaf(cK[t][w + u], dn[u], pred);
+        dn[t] = lane_value(bl, t) * (LdsRead<IT>::one(Vs + (long)t * VV * 16, vr) - pred);
+        float out = fmaf(G, pq[t][j], hist_q[t]);
+#pragma unroll
+        for (int u = 0; u <= t; ++u) out = fmaf(cQ[t][w + u], dn[u], out);
+        if (writer) {
+          Elt<OT>::store1(a.o, ((long)(b * T + t) * HV + hv) * V + vr, a.scale * out);
+          Ds[(w + t) * V + vr] = dn[t];
+        }
+      }
+    }
+  }
+  __syncthreads();  // the drafts' d rows are in LDS
+
+  // ---- 5. ring entries w..w+T-1: d, k (one writer per key head), g, v, beta
+  const bool k_writer = (hv % a.vpk) == 0;
+  for (int e = tid; e < T * (DV + QV + VV); e += NT) {
+    const int t = e / (DV + QV + VV);
+    const int r = e - t * (DV + QV + VV);
+    const int p = w + t;
+    if (r < DV) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(lds + ((long)oD + p * DV + r) * 16);
+      st16(a.d_ring, (dring0 + (long)p * V) * 4 + r * 16, x);
+    } else if (r < DV + QV) {
+      if (k_writer) {
+        const int cc = r - DV;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(Ks + ((long)p * QV + cc) * 16);
+        st16(a.k_ring, (kring0 + (long)p * K) * kIo + cc * 16, x);
+      }
+    } else {
+      const int cc = r - DV - QV;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(Vs + ((long)t * VV + cc) * 16);
+      st16(a.v_ring, (dring0 + (long)p * V) * kIo + cc * 16, x);
+    }
+  }
+  if (wave == 0) {
+    if (lane >= w && lane < w + T) a.g_ring[gring0 + lane] = gl;
+    if (lane < T) a.beta_ring[gring0 + w + lane] = bl;
+  }
+}
+
+// Commit LDS, 16-byte chunks: [k rows 0..L-1 | v rows 0..L-1]; then 2*V
+// floats for the d of the step in flight (double buffered).
+template <typename IT, int V, int K>
+struct CommitStage {
+  static constexpr int IV = Elt<IT>::kPer16;
+  static constexpr int QV = K / IV;
+  static constexpr int VV = V / IV;
+  static constexpr int oV(int L) { return L * QV; }
+  static constexpr size_t bytes(int L) { return (size_t)L * (QV + VV) * 16 + 2 * V * 4; }
+};
+
+template <typename IT, int V, int K>
+__global__ void __launch_bounds__((GdnShape<V, K, false>::NT)) gdn_spec_commit_kernel(const SpecArgs a) {
+  using GS = GdnShape<V, K, false>;
+  using SG = CommitStage<IT, V, K>;
+  constexpr int SV = GS::SV, LPR = GS::LPR, NT = GS::NT, ITEMS = GS::ITEMS, RPI = GS::RPI;
+  constexpr int QV = SG::QV, VV = SG::VV;
+  constexpr long kIo = sizeof(IT);
+  using RR = RowReduce<ITEMS, LPR>;
+
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int HV = a.v_heads, HK = a.k_heads, T = a.n_draft, L = a.ring_len;
+  const int tile = xcd_tile(blockIdx.x, gridDim.x);
+  const int b = tile / HV;
+  const int hv = tile - b * HV;
+  const int hk = hv / a.vpk;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int s = a.slot_idx[b];
+  const int acc = a.accepted[b];
+  int wn = a.write_pos[b] + acc;
+  int st = 0;
+  if (acc < 0 || acc > T || wn < 0 || wn > L) {
+    st |= RSSM_ST_RING_OVERFLOW;
+    wn = wn < 0 ? 0 : (wn > L ? L : wn);
+  }
+  const bool bad_slot = s < 0 || s >= a.num_slots;
+  if (bad_slot) st |= RSSM_ST_BAD_SLOT;
+  const bool flush = !bad_slot && (wn + T > L || (a.force_flush && a.force_flush[b]));
+  if (hv == 0 && tid == 0) {
+    if (a.next_write_pos) a.next_write_pos[b] = flush ? 0 : wn;
+    if (a.flushed) a.flushed[b] = flush ? 1 : 0;
+    if (st && a.status) atomicOr(a.status, st);
+  }
+  if (!flush || wn == 0) return;
+
+  // ---- exact fold: the recurrence over entries 0..wn-1 from their raw inputs
+  char* const tptr = (char*)a.state + ((long)s * HV + hv) * (long)V * K * 4;
+  const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(V * K * 4));
+  const uint32_t lane_off = tid * 16;
+  u32x4 sv[ITEMS];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
+  const long kring0 = ((long)s * HK + hk) * (long)L * K;
+  const long vring0 = ((long)s * HV + hv) * (long)L * V;
+  const long gring0 = ((long)s * HV + hv) * L;
+  dma_rows(lds, 0, wn * QV, (const char*)a.k_ring + kring0 * kIo, wave, lane, NT);
+  dma_rows(lds, SG::oV(L), wn * VV, (const char*)a.v_ring + vring0 * kIo, wave, lane, NT);
+  const float gl = lane < wn ? a.g_ring[gring0 + lane] : 1.f;
+  const float bl = lane < wn ? a.beta_ring[gring0 + lane] : 0.f;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const char* Ks = lds;
+  const char* Vs = lds + (long)SG::oV(L) * 16;
+  float* dbuf = reinterpret_cast<float*>(lds + (size_t)L * (QV + VV) * 16);
+
+  const int c = tid % LPR;
+  const int prow = tid / LPR;
+  float S[ITEMS][SV];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) Elt<float>::unpack(sv[it], S[it]);
+  const bool writer = (c % RR::DUP) == 0;
+  for (int i = 0; i < wn; ++i) {
+    const float gi = lane_value(gl, i), bi = lane_value(bl, i);
+    float kseg[SV];
+    LdsRead<IT>::template seg<SV>(Ks + (long)i * QV * 16, c * SV, kseg);
+    float part[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      float x = 0.f;
+#pragma unroll
+      for (int j = 0; j < SV; ++j) {
+        S[it][j] *= gi;
+        x = fmaf(S[it][j], kseg[j], x);
+      }
+      part[it] = x;
+    }
+    RR::run(part, tid);
+    float* db = dbuf + (i & 1) * V;
+#pragma unroll
+    for (int j = 0; j < RR::NF; ++j) {
+      const int vr = RR::item(j, tid) * RPI + prow;
+      if (writer) db[vr] = bi * (LdsRead<IT>::one(Vs + (long)i * VV * 16, vr) - part[j]);
+    }
+    __syncthreads();  // d of entry i; the other buffer is free for entry i+1
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const float dv = db[it * RPI + prow];
+#pragma unroll
+      for (int j = 0; j < SV; ++j) S[it][j] = fmaf(dv, kseg[j], S[it][j]);
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it)
+    st16_stream(tptr, (long)lane_off + it * NT * 16, Elt<float>::pack(S[it]));
+}
+
+template <typename IT, typename OT, int V, int K>
+static int launch_verify(const SpecArgs& a, int batch, hipStream_t stream) {
+  const size_t lds = (size_t)VerifyStage<IT, V, K>::chunks(a.n_draft, a.ring_len) * 16;
+  const size_t fixed = (2 * kMaxDraft * 64 + kMaxDraft) * sizeof(float);
+  if (lds + fixed > kMaxLds) return RSSM_ESHAPE;  // staged rows must fit one workgroup's LDS
+  return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K>),
+                       (unsigned)((long)batch * a.v_heads), GdnShape<V, K, true>::NT, lds, stream,
+                       a);
+}
+
+template <typename IT, int V, int K>
+static int launch_commit(const SpecArgs& a, int batch, hipStream_t stream) {
+  const size_t lds = CommitStage<IT, V, K>::bytes(a.ring_len);
+  if (lds > kMaxLds) return RSSM_ESHAPE;
+  return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_commit_kernel<IT, V, K>),
+                       (unsigned)((long)batch * a.v_heads), GdnShape<V, K, false>::NT, lds, stream,
+                       a);
+}
+
+template <typename IT, typename OT>
+static int verify_shape(const SpecArgs& a, const rssm_gdn_dims& d, hipStream_t s) {
+  if (d.dv == 128 && d.dk == 128) return launch_verify<IT, OT, 128, 128>(a, d.batch, s);
+  if (d.dv == 64 && d.dk == 64) return launch_verify<IT, OT, 64, 64>(a, d.batch, s);
+  if (d.dv == 128 && d.dk == 64) return launch_verify<IT, OT, 128, 64>(a, d.batch, s);
+  if (d.dv == 64 && d.dk == 128) return launch_verify<IT, OT, 64, 128>(a, d.batch, s);
+  return RSSM_ESHAPE;
+}
+
+template <typename IT>
+static int commit_shape(const SpecArgs& a, const rssm_gdn_dims& d, hipStream_t s) {
+  if (d.dv == 128 && d.dk == 128) return launch_commit<IT, 128, 128>(a, d.batch, s);
+  if (d.dv == 64 && d.dk == 64) return launch_commit<IT, 64, 64>(a, d.batch, s);
+  if (d.dv == 128 && d.dk == 64) return launch_commit<IT, 128, 64>(a, d.batch, s);
+  if (d.dv == 64 && d.dk == 128) return launch_commit<IT, 64, 128>(a, d.batch, s);
+  return RSSM_ESHAPE;
+}
+
+static int spec_check(const rssm_gdn_dims* d, int32_t n_draft) {
+  if (!d) return RSSM_EINVAL;
+  if (d->batch < 0 || d->k_heads < 1 || d->v_heads < 1 || d->v_heads % d->k_heads ||
+      d->num_slots < 1)
+    return RSSM_EINVAL;
+  if ((long)d->batch * d->v_heads > 0x7fffffffL) return RSSM_EINVAL;
+  if (d->state_dtype != RSSM_F32 || !valid_dtype(d->io_dtype) || !valid_dtype(d->out_dtype))
+    return RSSM_EDTYPE;
+  if (!((d->dk == 64 || d->dk == 128) && (d->dv == 64 || d->dv == 128))) return RSSM_ESHAPE;
+  if (n_draft < 1 || n_draft > kMaxDraft) return RSSM_ESHAPE;
+  if (d->ring_len < 2 * n_draft || d->ring_len > 64) return RSSM_ESHAPE;
+  return RSSM_OK;
+}
+
+static SpecArgs spec_args(const rssm_gdn_dims* d, int32_t n_draft) {
+  SpecArgs a{};
+  a.k_heads = d->k_heads;
+  a.v_heads = d->v_heads;
+  a.vpk = d->v_heads / d->k_heads;
+  a.ring_len = d->ring_len;
+  a.num_slots = d->num_slots;
+  a.n_draft = n_draft;
+  a.scale = d->scale > 0.f ? d->scale : 1.0f / sqrtf((float)d->dk);
+  return a;
+}
+
+}  // namespace rssm
+
+using namespace rssm;
+
+extern "C" int replayssm_gdn_spec_verify(const rssm_gdn_dims* dims, int32_t n_draft,
+                                         const void* state, float* d_ring, void* k_ring,
+                                         float* g_ring, void* v_ring, float* beta_ring,
+                                         const int32_t* slot_idx, const int32_t* write_pos,
+                                         const void* q, const void* k, const void* v,
+                                         const float* g, const float* beta, void* o,
+                                         int32_t* status, hipStream_t stream) {
+  int rc = spec_check(dims, n_draft);
+  if (rc) return rc;
+  if (dims->batch == 0) return RSSM_OK;
+  if (!state || !d_ring || !k_ring || !g_ring || !v_ring || !beta_ring || !slot_idx ||
+      !write_pos || !q || !k || !v || !g || !beta || !o)
+    return RSSM_EINVAL;
+  if (!aligned16(state) || !aligned16(d_ring) || !aligned16(k_ring) || !aligned16(v_ring) ||
+      !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return RSSM_EINVAL;
+  SpecArgs a = spec_args(dims, n_draft);
+  a.state = const_cast<float*>(static_cast<const float*>(state));
+  a.d_ring = d_ring;
+  a.k_ring = k_ring;
+  a.g_ring = g_ring;
+  a.v_ring = v_ring;
+  a.beta_ring = beta_ring;
+  a.slot_idx = slot_idx;
+  a.write_pos = write_pos;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.o = o;
+  a.status = status;
+  switch (dims->io_dtype * 2 + dims->out_dtype) {
+    case 0: return verify_shape<float, float>(a, *dims, stream);
+    case 1: return verify_shape<float, bf16>(a, *dims, stream);
+    case 2: return verify_shape<bf16, float>(a, *dims, stream);
+    case 3: return verify_shape<bf16, bf16>(a, *dims, stream);
+  }
+  return RSSM_EDTYPE;
+}
+
+extern "C" int replayssm_gdn_spec_commit(const rssm_gdn_dims* dims, int32_t n_draft, void* state,
+                                         const void* k_ring, const float* g_ring,
+                                         const void* v_ring, const float* beta_ring,
+                                         const int32_t* slot_idx, const int32_t* write_pos,
+                                         const int32_t* accepted, const uint8_t* force_flush,
+                                         int32_t* next_write_pos, uint8_t* flushed,
+                                         int32_t* status, hipStream_t stream) {
+  int rc = spec_check(dims, n_draft);
+  if (rc) return rc;
+  if (dims->batch == 0) return RSSM_OK;
+  if (!state || !k_ring || !g_ring || !v_ring || !beta_ring || !slot_idx || !write_pos ||
+      !accepted || !next_write_pos)
+    return RSSM_EINVAL;
+  if (!aligned16(state) || !aligned16(k_ring) || !aligned16(v_ring)) return RSSM_EINVAL;
+  if ((const void*)next_write_pos == (const void*)write_pos) return RSSM_EINVAL;
+  SpecArgs a = spec_args(dims, n_draft);
+  a.state = static_cast<float*>(state);
+  a.k_ring = const_cast<void*>(k_ring);
+  a.g_ring = const_cast<float*>(g_ring);
+  a.v_ring = const_cast<void*>(v_ring);
+  a.beta_ring = const_cast<float*>(beta_ring);
+  a.slot_idx = slot_idx;
+  a.write_pos = write_pos;
+  a.accepted = accepted;
+  a.force_flush = force_flush;
+  a.next_write_pos = next_write_pos;
+  a.flushed = flushed;
+  a.status = status;
+  switch (dims->io_dtype) {
+    case RSSM_F32: return commit_shape<float>(a, *dims, stream);
+    case RSSM_BF16: return commit_shape<bf16>(a, *dims, stream);
+  }
+  return RSSM_EDTYPE;
+}

@@ -30,7 +30,7 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = {
     "mamba2_decode_kernel": ("mamba2_kernel.hpp", "mamba2_decode.hip", "rssm_device.hpp",
                              "rssm_host.hpp"),
-    "gdn_decode_kernel": ("gdn_decode.hip", "rssm_device.hpp", "rssm_host.hpp"),
+    "gdn_decode_kernel": ("gdn_common.hpp", "gdn_decode.hip", "rssm_device.hpp", "rssm_host.hpp"),
 }
 
 

@@ -1,0 +1,138 @@
+"""GDN speculative verify and commit on the GPU against the float64 oracle:
+rounds of verify -> random acceptance -> commit (with exact folds whenever the
+next verify would not fit, and forced folds), checking every draft output,
+every cursor and every folded state."""
+
+import numpy as np
+import pytest
+import torch
+
+import linear_recurrence_amd as R
+from oracle import gdn_spec as OS
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+
+
+def _unit(rng, shape):
+    a = rng.normal(size=shape)
+    return a / np.linalg.norm(a, axis=-1, keepdims=True)
+
+
+def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32):
+    print(f"case: spec nb={nb} HK={HK} HV={HV} K={K} V={V} L={L} T={T} io={io}", flush=True)
+    rng = np.random.default_rng(seed)
+    dev = torch.device("cuda:0")
+    ns = nb + 3
+    slots = rng.permutation(ns)[:nb].astype(np.int32)
+    pool = rng.normal(0, 0.1, (ns, HV, V, K)).astype(np.float32)
+    st = torch.tensor(pool, device=dev)
+    dr = torch.full((ns, HV, L, V), float("nan"), device=dev)
+    kr = torch.full((ns, HK, L, K), float("nan"), dtype=io, device=dev)
+    gr = torch.full((ns, HV, L), float("nan"), device=dev)
+    vr = torch.full((ns, HV, L, V), float("nan"), dtype=io, device=dev)
+    br = torch.full((ns, HV, L), float("nan"), device=dev)
+    wp = torch.zeros(nb, dtype=torch.int32, device=dev)
+    nwp = torch.empty_like(wp)
+    fl = torch.empty(nb, dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    sl = torch.tensor(slots, device=dev)
+    sample = sorted(set(sample))
+    k_ = len(sample)
+    o_pool = pool[slots[sample]].astype(np.float64)
+    o_rings = [np.full((k_, HV, L, V), np.nan), np.full((k_, HK, L, K), np.nan),
+               np.full((k_, HV, L), np.nan), np.full((k_, HV, L, V), np.nan),
+               np.full((k_, HV, L), np.nan)]
+    o_sl = np.arange(k_)
+    o_wp = np.zeros(k_, np.int32)
+    fp32 = io == torch.float32
+    folds = 0
+    for r in range(rounds):
+        q = torch.tensor(_unit(rng, (nb, T, HK, K)), dtype=io, device=dev)
+        k = torch.tensor(_unit(rng, (nb, T, HK, K)), dtype=io, device=dev)
+        v = torch.tensor(rng.normal(size=(nb, T, HV, V)), dtype=io, device=dev)
+        g = torch.tensor(np.exp(-np.log1p(np.exp(rng.normal(size=(nb, T, HV))))),
+                         dtype=torch.float32, device=dev)
+        beta = torch.tensor(1 / (1 + np.exp(-rng.normal(size=(nb, T, HV)))),
+                            dtype=torch.float32, device=dev)
+        o = R.replayssm_gdn_spec_verify(st, dr, kr, gr, vr, br, sl, wp, q, k, v, g, beta,
+                                        status=status, out_dtype=out)
+        npv = lambda t: t[sample].double().cpu().numpy()
+        o_ref, ost = OS.gdn_spec_verify(o_pool, *o_rings, o_sl, o_wp, npv(q), npv(k), npv(v),
+                                        npv(g), npv(beta))
+        assert ost == 0
+        got = o[sample].double().cpu().numpy()
+        d = np.abs(got - o_ref)
+        if fp32 and out == torch.float32:
+            err = d.max() / np.abs(o_ref).max()
+            assert err <= 2e-5, f"round {r}: o error {err:.2e}"
+        else:
+            bound = np.maximum(1e-2, np.abs(o_ref) * 2**-7)
+            assert (d <= bound).all(), f"round {r}: o error {d.max():.2e}"
+        acc = rng.integers(0, T + 1, nb).astype(np.int32)
+        force = (rng.random(nb) < 0.1).astype(np.uint8)
+        R.replayssm_gdn_spec_commit(st, kr, gr, vr, br, sl, wp, torch.tensor(acc, device=dev),
+                                    T, nwp, force_flush=torch.tensor(force, device=dev),
+                                    flushed=fl, status=status)
+        o_wp, o_fl, ost = OS.gdn_spec_commit(o_pool, *o_rings[1:], o_sl, o_wp, acc[sample], T,
+                                             force_flush=force[sample], state_dtype="f32")
+        assert ost == 0
+        # cursors of every row follow the commit rule
+        w_all = wp.cpu().numpy() + acc
+        fl_ref = ((w_all + T > L) | (force != 0)).astype(np.uint8)
+        np.testing.assert_array_equal(fl.cpu().numpy(), fl_ref)
+        np.testing.assert_array_equal(nwp.cpu().numpy(), np.where(fl_ref, 0, w_all))
+        np.testing.assert_array_equal(nwp.cpu().numpy()[sample], o_wp)
+        for j, row in enumerate(sample):
+            if o_fl[j]:
+                folds += 1
+                gs = st[int(slots[row])].double().cpu().numpy()
+                e = np.abs(gs - o_pool[j]).max()
+                lim = 2e-5 * np.abs(o_pool[j]).max() if fp32 else 1e-2
+                assert e <= lim, f"round {r} row {row}: folded state error {e:.2e}"
+        wp, nwp = nwp, wp
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    assert folds > 0
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_spec_small(io, K, V):
+    run_spec(5, 2, 4, K, V, 8, 3, io, 14, range(5), seed=K + V + (io == torch.bfloat16))
+
+
+@pytest.mark.parametrize("L,T", [(2, 1), (16, 8), (64, 8), (20, 5)])
+def test_spec_ring_lengths(L, T):
+    run_spec(3, 1, 2, 128, 128, L, T, torch.bfloat16, max(6, 3 * L // T), range(3), seed=L * 7 + T)
+
+
+def test_spec_full_size_bf16_output():
+    """256 rows, 16 key / 32 value heads, K = V = 128, L = 16, 4 drafts."""
+    run_spec(256, 16, 32, 128, 128, 16, 4, torch.bfloat16, 12, [0, 99, 200, 255], seed=4,
+             out=torch.bfloat16)
+
+
+def test_spec_bad_cursor_is_refused():
+    print("case: spec bad cursor", flush=True)
+    dev = torch.device("cuda:0")
+    HK, HV, K, V, L, T = 1, 2, 64, 64, 8, 4
+    st = torch.zeros((2, HV, V, K), device=dev)
+    rings = (torch.zeros((2, HV, L, V), device=dev), torch.zeros((2, HK, L, K), device=dev),
+             torch.zeros((2, HV, L), device=dev), torch.zeros((2, HV, L, V), device=dev),
+             torch.zeros((2, HV, L), device=dev))
+    sl = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+    wp = torch.tensor([0, 5], dtype=torch.int32, device=dev)   # row 1: 5 + 4 > 8
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    q = torch.ones((2, T, HK, K), device=dev) / 8
+    v = torch.ones((2, T, HV, V), device=dev)
+    gb = torch.full((2, T, HV), 0.5, device=dev)
+    o = R.replayssm_gdn_spec_verify(st, *rings, sl, wp, q, q, v, gb, gb, status=status)
+    torch.cuda.synchronize()
+    assert status.item() & R.ST_RING_OVERFLOW
+    assert torch.isnan(o[1]).all() and torch.isfinite(o[0]).all()

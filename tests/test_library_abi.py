@@ -75,6 +75,16 @@ def test_host_validation_rejects_bad_arguments_without_a_gpu():
     assert call(dims=dict(rounding=1, state_dtype=1, batch=0)) == 0
     gd = R.GdnDims(2, 1, 2, 128, 128, 4, 4, 1, 1, 1, 0.0)
     assert lib.gdn_standard_decode(ctypes.byref(gd), *([V(0x1000)] * 8), None, None) == -2
+    gd = R.GdnDims(2, 1, 2, 128, 128, 8, 4, 0, 1, 1, 0.0)
+    sv = [V(0x1000)] * 14                     # state .. o
+    assert lib.replayssm_gdn_spec_verify(ctypes.byref(gd), 0, *sv, None, None) == -4   # T < 1
+    assert lib.replayssm_gdn_spec_verify(ctypes.byref(gd), 5, *sv, None, None) == -4   # 2T > L
+    assert lib.replayssm_gdn_spec_verify(ctypes.byref(gd), 4, *sv[:13], None, None, None) == -1
+    cm = [V(0x1000)] * 6                      # state .. slot_idx
+    assert lib.replayssm_gdn_spec_commit(ctypes.byref(gd), 4, *cm, V(0x1000), None, None,
+                                         V(0x2000), None, None, None) == -1        # no accepted
+    assert lib.replayssm_gdn_spec_commit(ctypes.byref(gd), 4, *cm, V(0x3000), V(0x1000), None,
+                                         V(0x3000), None, None, None) == -1        # aliasing
     d = R.Dims(**good)
     assert lib.replayssm_ring_reset(ctypes.byref(d), None, None, None, 0, None, None) == 0
     assert lib.replayssm_ring_reset(ctypes.byref(d), None, None, None, -1, None, None) == -1
