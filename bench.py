@@ -15,7 +15,8 @@ read+write update (ssu_standard_decode) on the same workload; both again
 with stochastic rounding of the bf16 write-back; one tensor-parallel rank's
 share of the layer (10 of 80 heads); the GDN replay/standard decode at
 batch 256 (16 key / 32 value heads, K = V = 128, L = 16, bf16 q/k/v, fp32
-state); the host metadata builder; and the float64 CPU oracle on a bounded
+state) and its speculative verify + commit with 4 drafts per round; the host
+metadata builder; and the float64 CPU oracle on a bounded
 sample (``cpu_baseline``).
 
 Roofline: algorithmic bytes per launch (checkpoint reads, ring reads of the
@@ -278,6 +279,90 @@ def bench_gdn(wl, layers, steps, warmup, dev):
     return res
 
 
+def bench_gdn_spec(wl, T, layers, rounds, warmup, dev):
+    """GDN speculative decoding from the ring: per round one verify of T drafts
+    per row and one commit (accepted counts from a fixed seeded pattern; rows
+    whose next verify would not fit fold their ring by the exact recurrence).
+    Algorithmic bytes are counted per launch from every row's cursor."""
+    import linear_recurrence_amd as R
+    HK, HV, K, V, L, nb = wl.k_heads, wl.v_heads, wl.dk, wl.dv, wl.ring_len, wl.batch
+    ns = 2 * nb
+    io = torch.bfloat16
+    sio = 2
+    rng = np.random.default_rng(5)
+    from workloads import device_normal_
+    lay = []
+    for l in range(layers):
+        st = torch.empty((ns, HV, V, K), dtype=torch.float32, device=dev)
+        device_normal_(st, 0.1, 300 + l)
+        lay.append(dict(st=st, dr=torch.zeros((ns, HV, L, V), device=dev),
+                        kr=torch.zeros((ns, HK, L, K), dtype=io, device=dev),
+                        gr=torch.zeros((ns, HV, L), device=dev),
+                        vr=torch.zeros((ns, HV, L, V), dtype=io, device=dev),
+                        br=torch.zeros((ns, HV, L), device=dev),
+                        wp=torch.zeros(nb, dtype=torch.int32, device=dev),
+                        nwp=torch.zeros(nb, dtype=torch.int32, device=dev), w=np.zeros(nb, np.int64)))
+    slots = torch.tensor(rng.permutation(ns)[:nb].astype(np.int32), device=dev)
+
+    def unit(shape):
+        a = torch.randn(shape, device=dev)
+        return (a / a.norm(dim=-1, keepdim=True)).to(io)
+    torch.manual_seed(5)
+    inputs = [dict(q=unit((nb, T, HK, K)), k=unit((nb, T, HK, K)),
+                   v=torch.randn((nb, T, HV, V), device=dev).to(io),
+                   g=torch.exp(-torch.nn.functional.softplus(torch.randn((nb, T, HV), device=dev))),
+                   beta=torch.sigmoid(torch.randn((nb, T, HV), device=dev))) for _ in range(4)]
+    accepts = [rng.integers(0, T + 1, nb).astype(np.int32) for _ in range(8)]
+    acc_t = [torch.tensor(a, device=dev) for a in accepts]
+    o = torch.empty((nb, T, HV, V), dtype=io, device=dev)
+    vpk = HV // HK
+    tile = V * K * 4
+    entry = V * 4 + K * sio / vpk + 4                    # d, k (shared per key head), g
+    raw = V * sio + K * sio / vpk + 8                    # v, k, g, beta for the exact fold
+    inp = T * (2 * K * sio / vpk + V * sio + 8 + V * sio)  # q, k, v, g, beta in; o out
+    bytes_total = [0.0]
+
+    def rnd(i, count=True):
+        d = lay[i % layers]
+        inp_i = inputs[i % 4]
+        R.replayssm_gdn_spec_verify(d["st"], d["dr"], d["kr"], d["gr"], d["vr"], d["br"], slots,
+                                    d["wp"], inp_i["q"], inp_i["k"], inp_i["v"], inp_i["g"],
+                                    inp_i["beta"], o=o)
+        a = accepts[i % 8]
+        R.replayssm_gdn_spec_commit(d["st"], d["kr"], d["gr"], d["vr"], d["br"], slots, d["wp"],
+                                    acc_t[i % 8], T, d["nwp"])
+        d["wp"], d["nwp"] = d["nwp"], d["wp"]
+        w = d["w"]
+        wn = w + a
+        fold = wn + T > L
+        if count:
+            per_row = (tile + w * entry + T * (entry + V * sio + 4) + inp + 4) * HV \
+                + np.where(fold, (2 * tile + wn * raw) * HV, 0) + 12
+            bytes_total[0] += float(per_row.sum())
+        d["w"] = np.where(fold, 0, wn)
+
+    for i in range(warmup):
+        rnd(i, False)
+    torch.cuda.synchronize()
+    t = time_region(lambda i: rnd(warmup + i), rounds, 0)
+    for l in range(layers):
+        assert np.array_equal(lay[l]["wp"].cpu().numpy(), lay[l]["w"]), "spec cursor drift"
+    acc_mean = float(np.mean([a.mean() for a in accepts]))
+    res = {
+        "workload": f"gdn_spec_b{nb}_hk{HK}_hv{HV}_k{K}_L{L}_T{T}",
+        "drafts_per_round": T, "mean_accepted": acc_mean,
+        "rounds_per_s": rounds / t, "us_per_round": t / rounds * 1e6,
+        "verified_tokens_per_s": nb * T * rounds / t,
+        "committed_tokens_per_s": nb * acc_mean * rounds / t,
+        "GBps": bytes_total[0] / t / 1e9, "frac": bytes_total[0] / t / 1e9 / PEAK_HBM_GBPS,
+        "bytes_per_round": bytes_total[0] / rounds,
+        "recurrent_verify_bytes_per_round": float(nb * HV * (1 + T) * tile),
+    }
+    del lay
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(wl, rows, steps):
     """The float64 oracle's replay step on a bounded sample of the workload:
     `rows` rows of the batch for `steps` steps from its first (desync) warm-up
@@ -426,6 +511,10 @@ def main():
         gdn = bench_gdn(GDN, args.layers, args.steps, args.warmup, dev)
         print(f"[bench] gdn done: {gdn['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
               flush=True)
+    spec = None
+    if not args.no_gdn:
+        spec = bench_gdn_spec(GDN, 4, args.layers, 256, 16, dev)
+        print(f"[bench] gdn spec done: {spec['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
     cpu = None
     if not args.no_cpu:
         cpu = cpu_baseline(wl, args.cpu_rows, args.cpu_steps)
@@ -475,6 +564,7 @@ def main():
         },
         "speedup_vs_standard": m["replay_updates_per_s"] / m["standard_updates_per_s"],
         "gdn": gdn,
+        "gdn_spec": spec,
         "stochastic_rounding": m.get("stochastic_rounding"),
         "tp8_share": tp,
         "metadata_builder": metadata_rate(wl.batch, wl.ring_len),

@@ -15,9 +15,10 @@
 // Verify mapping: one workgroup per (row, value head) fp32 [V, K] tile, the
 // tile read once into registers; q, v of the T drafts, the k rows of the
 // committed entries and of the drafts, and the committed d rows staged in
-// LDS by direct-to-LDS loads.  Wave 0 forms, per draft t at ring position
-// p = w + t, the gate products (DPP suffix products over the lanes holding
-// g_0..g_p) and the weighted dots gamma_i*(k_i.k_p), gamma_i*(k_i.q_t);
+// LDS by direct-to-LDS loads.  The waves form, per draft t at ring position
+// p = w + t (one draft per wave at a time), the gate products (DPP suffix
+// products over the lanes holding g_0..g_p) and the weighted dots
+// gamma_i*(k_i.k_p), gamma_i*(k_i.q_t);
 // every lane forms S0.k_p and S0.q_t for its state rows (2T butterfly row
 // reductions) and then walks the drafts in order, keeping the new d values
 // of its rows in registers.  The drafts' (d, k, g, v, beta) are written to
@@ -164,11 +165,13 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   const char* Ks = lds + (long)oK * 16;
   float* Ds = reinterpret_cast<float*>(lds + (long)oD * 16);
 
-  // ---- 2. wave 0: gate products and weighted dots of every draft
-  if (wave == 0) {
+  // ---- 2. gate products and weighted dots of every draft (draft t on wave
+  // t mod (waves))
+  {
     constexpr int EPL = K / 16;
+    constexpr int NW = NT / 64;
     const int q16 = lane & 15;
-    for (int t = 0; t < T; ++t) {
+    for (int t = wave; t < T; t += NW) {
       const int p = w + t;
       const float gt = lane <= p ? gl : 1.f;
       const float gam = L <= 16 ? row16_suffix_product_exclusive(gt)
