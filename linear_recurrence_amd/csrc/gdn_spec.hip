@@ -80,6 +80,19 @@ struct VerifyStage {
   static constexpr int oK(int T) { return T * (QV + VV); }
   static constexpr int oD(int T, int L) { return oK(T) + ((L + 7) & ~7) * QV; }
   static constexpr int chunks(int T, int L) { return oD(T, L) + L * DV; }
+  // matrix-core variant: S0 . (k, q) products [V][16] fp32 after the d rows
+  static constexpr int oP(int T, int L) { return chunks(T, L); }
+  static constexpr int chunks_mfma(int T, int L) { return chunks(T, L) + V * 4; }
+};
+
+// Matrix-core split of the verify's S0 products (bf16 inputs): a wave owns
+// VBW blocks of 16 state rows by all KB blocks of 32 columns.
+template <int V, int K, int NT>
+struct VerifyMfma {
+  static constexpr int NW = NT / 64;
+  static constexpr int KB = K / 32;
+  static constexpr int VBW = V / 16 / NW;
+  static constexpr int NBLK = VBW * KB;  // blocks per wave, two 16-byte loads each
 };
 
 // 16-byte chunks [c0, c0+n) of LDS from global memory, one wave-wide
@@ -92,18 +105,25 @@ __device__ static inline void dma_rows(char* lds, int c0, int n, const char* src
   }
 }
 
-template <typename IT, typename OT, int V, int K>
+template <typename IT, typename OT, int V, int K, bool MF>
 __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_kernel(const SpecArgs a) {
   using GS = GdnShape<V, K, true>;
   using SG = VerifyStage<IT, V, K>;
+  using VM = VerifyMfma<V, K, GS::NT>;
+  static_assert(!MF || (std::is_same<IT, bf16>::value && 2 * VM::NBLK == GS::ITEMS &&
+                        VM::VBW >= 1),
+                "matrix-core verify: bf16 inputs, the tile in 16x32 blocks");
   constexpr int SV = GS::SV, LPR = GS::LPR, NT = GS::NT, ITEMS = GS::ITEMS, RPI = GS::RPI;
   constexpr int QV = SG::QV, VV = SG::VV, DV = SG::DV;
   constexpr long kIo = sizeof(IT);
   using RR = RowReduce<ITEMS, LPR>;
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
-  __shared__ float cK[kMaxDraft][64];  // gamma_{i,t} * (k_i . k_{w+t}), i < w+t
-  __shared__ float cQ[kMaxDraft][64];  // gamma_{i,t} * (k_i . q_t),     i <= w+t
+  // [i][t]: gamma_{i,t} (k_i . k_{w+t}) for i < w+t, gamma_{i,t} (k_i . q_t)
+  // for i <= w+t; entry-major, so one entry's weights for all drafts are one
+  // vector read
+  __shared__ __attribute__((aligned(16))) float cK[64][kMaxDraft];
+  __shared__ __attribute__((aligned(16))) float cQ[64][kMaxDraft];
   __shared__ float gamS[kMaxDraft];    // Gamma_t = prod_{j <= w+t} g_j
 
   const int HV = a.v_heads, HK = a.k_heads, T = a.n_draft, L = a.ring_len;
@@ -134,8 +154,21 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(V * K * 4));
   const uint32_t lane_off = tid * 16;
   u32x4 sv[ITEMS];
+  if constexpr (MF) {
+    // block (vb, kb): lane l takes S0[16*vb + l%16][32*kb + 8*(l/16) .. +8],
+    // the B operand layout of the 16x16x32 product
+    const uint32_t voff = (uint32_t)(((lane & 15) * K + 8 * (lane >> 4)) * 4);
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
+    for (int jb = 0; jb < VM::NBLK; ++jb) {
+      const int vb = wave * VM::VBW + jb / VM::KB, kb = jb % VM::KB;
+      const uint32_t soff = (uint32_t)((16 * vb * K + 32 * kb) * 4);
+      sv[2 * jb] = bload16_nt(trs, voff, soff);
+      sv[2 * jb + 1] = bload16_nt(trs, voff, soff + 16);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
+  }
 
   const long kring0 = ((long)s * HK + hk) * (long)L * K;
   const long dring0 = ((long)s * HV + hv) * (long)L * V;
@@ -194,62 +227,29 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
           kq = a2;
         }
       }
-      cK[t][lane] = lane < p ? gam * kk : 0.f;
-      cQ[t][lane] = lane <= p ? gam * kq : 0.f;
+      cK[lane][t] = lane < p ? gam * kk : 0.f;
+      cQ[lane][t] = lane <= p ? gam * kq : 0.f;
     }
   }
   __syncthreads();
 
-  // ---- 3. S0 . k_{w+t} and S0 . q_t for this lane's state rows
-  const int c = tid % LPR;
-  const int prow = tid / LPR;
-  float pk[kMaxDraft][RR::NF], pq[kMaxDraft][RR::NF];
-#pragma unroll
-  for (int t = 0; t < kMaxDraft; ++t) {
-    if (t < T) {
-      float kseg[SV], qseg[SV];
-      LdsRead<IT>::template seg<SV>(Ks + (long)(w + t) * QV * 16, c * SV, kseg);
-      LdsRead<IT>::template seg<SV>(Qs + (long)t * QV * 16, c * SV, qseg);
-      float a1[ITEMS], a2[ITEMS];
-#pragma unroll
-      for (int it = 0; it < ITEMS; ++it) {
-        float sf[SV];
-        Elt<float>::unpack(sv[it], sf);
-        float x1 = 0.f, x2 = 0.f;
-#pragma unroll
-        for (int j = 0; j < SV; ++j) {
-          x1 = fmaf(sf[j], kseg[j], x1);
-          x2 = fmaf(sf[j], qseg[j], x2);
-        }
-        a1[it] = x1;
-        a2[it] = x2;
-      }
-      RR::run(a1, tid);
-      RR::run(a2, tid);
-#pragma unroll
-      for (int j = 0; j < RR::NF; ++j) {
-        pk[t][j] = a1[j];
-        pq[t][j] = a2[j];
-      }
-    }
-  }
-
-  // ---- 4. per state row, the drafts in order
-  const bool writer = (c % RR::DUP) == 0;
-#pragma unroll
-  for (int j = 0; j < RR::NF; ++j) {
-    const int vr = RR::item(j, tid) * RPI + prow;
+  // ---- 4 (per state row, the drafts in order), given S0.k_{w+t}, S0.q_t
+  auto draft_row = [&](int vr, const float* pkv, const float* pqv, bool writer) {
     float hist_k[kMaxDraft], hist_q[kMaxDraft];  // committed-entry terms per draft
 #pragma unroll
     for (int t = 0; t < kMaxDraft; ++t) hist_k[t] = hist_q[t] = 0.f;
     for (int i = 0; i < w; ++i) {
       const float di = Ds[i * V + vr];
+      float ck[kMaxDraft], cq[kMaxDraft];
 #pragma unroll
       for (int t = 0; t < kMaxDraft; ++t) {
-        if (t < T) {
-          hist_k[t] = fmaf(cK[t][i], di, hist_k[t]);
-          hist_q[t] = fmaf(cQ[t][i], di, hist_q[t]);
-        }
+        ck[t] = cK[i][t];
+        cq[t] = cQ[i][t];
+      }
+#pragma unroll
+      for (int t = 0; t < kMaxDraft; ++t) {  // sums past T are never used
+        hist_k[t] = fmaf(ck[t], di, hist_k[t]);
+        hist_q[t] = fmaf(cq[t], di, hist_q[t]);
       }
     }
     float dn[kMaxDraft];
@@ -258,18 +258,113 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
       dn[t] = 0.f;
       if (t < T) {
         const float G = gamS[t];
-        float pred = fmaf(G, pk[t][j], hist_k[t]);
+        float pred = fmaf(G, pkv[t], hist_k[t]);
 #pragma unroll
-        for (int u = 0; u < t; ++u) pred = fmaf(cK[t][w + u], dn[u], pred);
+        for (int u = 0; u < t; ++u) pred = fmaf(cK[w + u][t], dn[u], pred);
         dn[t] = lane_value(bl, t) * (LdsRead<IT>::one(Vs + (long)t * VV * 16, vr) - pred);
-        float out = fmaf(G, pq[t][j], hist_q[t]);
+        float out = fmaf(G, pqv[t], hist_q[t]);
 #pragma unroll
-        for (int u = 0; u <= t; ++u) out = fmaf(cQ[t][w + u], dn[u], out);
+        for (int u = 0; u <= t; ++u) out = fmaf(cQ[w + u][t], dn[u], out);
         if (writer) {
           Elt<OT>::store1(a.o, ((long)(b * T + t) * HV + hv) * V + vr, a.scale * out);
           Ds[(w + t) * V + vr] = dn[t];
         }
       }
+    }
+  };
+
+  if constexpr (MF) {
+    // ---- 3. D[m][v] = sum_k A[m][k] S0[v][k] on the matrix cores, with
+    // A = (k_w .. k_{w+T-1}, q_0 .. q_{T-1}, zero rows) exact in bf16 and S0
+    // split into bf16 hi + lo halves (two products per block)
+    const int m = lane & 15, g4 = lane >> 4;
+    const char* arow = m < T ? Ks + (long)(w + m) * QV * 16
+                             : (m < 2 * T ? Qs + (long)(m - T) * QV * 16 : nullptr);
+    u32x4 afr[VM::KB];
+#pragma unroll
+    for (int kb = 0; kb < VM::KB; ++kb)
+      afr[kb] = arow ? *reinterpret_cast<const u32x4*>(arow + (32 * kb + 8 * g4) * 2)
+                     : u32x4{0u, 0u, 0u, 0u};
+    f32x4 acc[VM::VBW];
+#pragma unroll
+    for (int j = 0; j < VM::VBW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int jb = 0; jb < VM::NBLK; ++jb) {
+      float f[8];
+      Elt<float>::unpack(sv[2 * jb], f);
+      Elt<float>::unpack(sv[2 * jb + 1], f + 4);
+      u32x4 hi, lo;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t h = bf16_pair(f[2 * q], f[2 * q + 1]);
+        hi[q] = h;
+        lo[q] = bf16_pair(f[2 * q] - __uint_as_float(h << 16),
+                          f[2 * q + 1] - __uint_as_float(h & 0xffff0000u));
+      }
+      const int j = jb / VM::KB, kb = jb % VM::KB;
+      acc[j] = mfma16x16x32_bf16(afr[kb], hi, acc[j]);
+      acc[j] = mfma16x16x32_bf16(afr[kb], lo, acc[j]);
+    }
+    // lane holds D[4*g4 + r][16*vb + m]: products of state row v in P[v][.]
+    float* Pm = reinterpret_cast<float*>(lds + (long)SG::oP(T, L) * 16);
+#pragma unroll
+    for (int j = 0; j < VM::VBW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Pm[(16 * (wave * VM::VBW + j) + m) * 16 + 4 * g4 + r] = acc[j][r];
+    __syncthreads();
+    for (int vr = tid; vr < V; vr += NT) {
+      float pkv[kMaxDraft], pqv[kMaxDraft];
+#pragma unroll
+      for (int t = 0; t < kMaxDraft; ++t) {
+        pkv[t] = t < T ? Pm[vr * 16 + t] : 0.f;
+        pqv[t] = t < T ? Pm[vr * 16 + T + t] : 0.f;
+      }
+      draft_row(vr, pkv, pqv, true);
+    }
+  } else {
+    // ---- 3. S0 . k_{w+t} and S0 . q_t for this lane's state rows
+    const int c = tid % LPR;
+    const int prow = tid / LPR;
+    float pk[kMaxDraft][RR::NF], pq[kMaxDraft][RR::NF];
+#pragma unroll
+    for (int t = 0; t < kMaxDraft; ++t) {
+      if (t < T) {
+        float kseg[SV], qseg[SV];
+        LdsRead<IT>::template seg<SV>(Ks + (long)(w + t) * QV * 16, c * SV, kseg);
+        LdsRead<IT>::template seg<SV>(Qs + (long)t * QV * 16, c * SV, qseg);
+        float a1[ITEMS], a2[ITEMS];
+#pragma unroll
+        for (int it = 0; it < ITEMS; ++it) {
+          float sf[SV];
+          Elt<float>::unpack(sv[it], sf);
+          float x1 = 0.f, x2 = 0.f;
+#pragma unroll
+          for (int j = 0; j < SV; ++j) {
+            x1 = fmaf(sf[j], kseg[j], x1);
+            x2 = fmaf(sf[j], qseg[j], x2);
+          }
+          a1[it] = x1;
+          a2[it] = x2;
+        }
+        RR::run(a1, tid);
+        RR::run(a2, tid);
+#pragma unroll
+        for (int j = 0; j < RR::NF; ++j) {
+          pk[t][j] = a1[j];
+          pq[t][j] = a2[j];
+        }
+      }
+    }
+    const bool writer = (c % RR::DUP) == 0;
+#pragma unroll
+    for (int j = 0; j < RR::NF; ++j) {
+      float pkv[kMaxDraft], pqv[kMaxDraft];
+#pragma unroll
+      for (int t = 0; t < kMaxDraft; ++t) {
+        pkv[t] = t < T ? pk[t][j] : 0.f;
+        pqv[t] = t < T ? pq[t][j] : 0.f;
+      }
+      draft_row(RR::item(j, tid) * RPI + prow, pkv, pqv, writer);
     }
   }
   __syncthreads();  // the drafts' d rows are in LDS
@@ -410,14 +505,26 @@ __global__ void __launch_bounds__((GdnShape<V, K, false>::NT)) gdn_spec_commit_k
     st16_stream(tptr, (long)lane_off + it * NT * 16, Elt<float>::pack(S[it]));
 }
 
+// bf16 inputs take the matrix-core products when their LDS fits; otherwise
+// (fp32 inputs, or the largest rings) the vector path.
 template <typename IT, typename OT, int V, int K>
 static int launch_verify(const SpecArgs& a, int batch, hipStream_t stream) {
-  const size_t lds = (size_t)VerifyStage<IT, V, K>::chunks(a.n_draft, a.ring_len) * 16;
+  using SG = VerifyStage<IT, V, K>;
+  constexpr int NT = GdnShape<V, K, true>::NT;
   const size_t fixed = (2 * kMaxDraft * 64 + kMaxDraft) * sizeof(float);
+  const unsigned grid = (unsigned)((long)batch * a.v_heads);
+  if constexpr (std::is_same<IT, bf16>::value &&
+                2 * VerifyMfma<V, K, NT>::NBLK == GdnShape<V, K, true>::ITEMS) {
+    const size_t lds = (size_t)SG::chunks_mfma(a.n_draft, a.ring_len) * 16;
+    if (lds + fixed <= kMaxLds)
+      return launch_kernel(
+          reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, true>), grid, NT,
+          lds, stream, a);
+  }
+  const size_t lds = (size_t)SG::chunks(a.n_draft, a.ring_len) * 16;
   if (lds + fixed > kMaxLds) return RSSM_ESHAPE;  // staged rows must fit one workgroup's LDS
-  return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K>),
-                       (unsigned)((long)batch * a.v_heads), GdnShape<V, K, true>::NT, lds, stream,
-                       a);
+  return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, false>),
+                       grid, NT, lds, stream, a);
 }
 
 template <typename IT, int V, int K>

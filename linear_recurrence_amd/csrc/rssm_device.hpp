@@ -286,6 +286,16 @@ template <> struct LdsRead<bf16> {
   }
 };
 
+// Matrix-core product D = A*B + C, 16x16 outputs, K = 32 bf16 (gfx950).
+// Lane l holds A[l%16][8*(l/16) + e] and B[8*(l/16) + e][l%16] (e = 0..7),
+// and receives D[4*(l/16) + r][l%16] (r = 0..3).
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ static inline f32x4 mfma16x16x32_bf16(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // Philox4x64-10 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as
 // easy as 1, 2, 3", SC 2011): a counter-based generator.  Each of the ten
 // rounds multiplies counter words 0 and 2 by the two round multipliers,
