@@ -28,6 +28,9 @@ Modules
               ReplaySSM ring replay with flush, cursor advance and ring reset.
 ``gdn``       gated delta rule: recurrence and ring replay.
 ``metadata``  host cursors of a step from token positions (decode base).
+``gdn_spec``  GDN speculative verify over drafts and commit with exact fold.
+``kda``       gated delta rule with a per-key-channel gate (KDA): recurrence
+              and ring replay.
 """
 
-from . import numerics, mamba2, gdn, metadata  # noqa: F401
+from . import numerics, mamba2, gdn, metadata, gdn_spec, kda  # noqa: F401
