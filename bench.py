@@ -15,7 +15,9 @@ read+write update (ssu_standard_decode) on the same workload; both again
 with stochastic rounding of the bf16 write-back; one tensor-parallel rank's
 share of the layer (10 of 80 heads); the GDN replay/standard decode at
 batch 256 (16 key / 32 value heads, K = V = 128, L = 16, bf16 q/k/v, fp32
-state) and its speculative verify + commit with 4 drafts per round; the host
+state) and its speculative verify + commit with 4 drafts per round; the KDA
+(per-key-channel gate) replay/standard decode at batch 256, 32 heads,
+K = V = 128, L = 16; the host
 metadata builder; and the float64 CPU oracle on a bounded
 sample (``cpu_baseline``).
 
@@ -225,9 +227,12 @@ def bench_gdn(wl, layers, steps, warmup, dev):
         st = torch.empty((ns, HV, V, K), dtype=torch.float32, device=dev)
         device_normal_(st, 0.1, 100 + l)
         states.append(st)
+    gsh = (K,) if wl.kda else ()  # per-entry gate: a [K] row (KDA) or a scalar (GDN)
+    rep_fn = R.replayssm_kda_decode if wl.kda else R.replayssm_gdn_decode
+    std_fn = R.kda_standard_decode if wl.kda else R.gdn_standard_decode
     dr = [torch.zeros((ns, HV, L, V), device=dev) for _ in range(layers)]
     kr = [torch.zeros((ns, HK, L, K), dtype=io, device=dev) for _ in range(layers)]
-    gr = [torch.zeros((ns, HV, L), device=dev) for _ in range(layers)]
+    gr = [torch.zeros((ns, HV, L) + gsh, device=dev) for _ in range(layers)]
     wp = [torch.zeros(nb, dtype=torch.int32, device=dev) for _ in range(layers)]
     fl = [torch.zeros(nb, dtype=torch.uint8, device=dev) for _ in range(layers)]
     nwp = [torch.empty_like(t) for t in wp]
@@ -239,17 +244,16 @@ def bench_gdn(wl, layers, steps, warmup, dev):
     def rep(i):
         l = i % layers
         inp = inputs[i % 8]
-        R.replayssm_gdn_decode(states[l], dr[l], kr[l], gr[l], slots, wp[l], fl[l], inp["q"],
-                               inp["k"], inp["v"], inp["g"], inp["beta"], o=o,
-                               next_write_pos=nwp[l], next_is_flush=nfl[l])
+        rep_fn(states[l], dr[l], kr[l], gr[l], slots, wp[l], fl[l], inp["q"], inp["k"],
+               inp["v"], inp["g"], inp["beta"], o=o, next_write_pos=nwp[l],
+               next_is_flush=nfl[l])
         wp[l], nwp[l] = nwp[l], wp[l]
         fl[l], nfl[l] = nfl[l], fl[l]
 
     def std(i):
         l = i % layers
         inp = inputs[i % 8]
-        R.gdn_standard_decode(states[l], slots, inp["q"], inp["k"], inp["v"], inp["g"],
-                              inp["beta"], o=o)
+        std_fn(states[l], slots, inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], o=o)
 
     # whole ring periods per layer keep the flush share exact (lock-step rows)
     steps_r = max(layers * L, (steps // (layers * L)) * layers * L)
@@ -258,8 +262,9 @@ def bench_gdn(wl, layers, steps, warmup, dev):
     t_std = time_region(std, steps, warmup)
     sio = _sizes(io)
     tile = HV * V * K * 4
-    entry = HV * V * 4 + HK * K * sio + HV * 4
-    inp_b = 2 * HK * K * sio + HV * V * sio + 2 * HV * 4 + HV * V * sio
+    gate = HV * K * 4 if wl.kda else HV * 4  # one entry's gates
+    entry = HV * V * 4 + HK * K * sio + gate
+    inp_b = 2 * HK * K * sio + HV * V * sio + gate + HV * 4 + HV * V * sio
     # lock-step rows: over a ring period the positions are 0..L-1 once each
     ring_reads = sum(range(L)) / L * entry
     per_row_rep = tile + ring_reads + (L - 1) / L * entry + tile / L + inp_b + 14
@@ -457,6 +462,7 @@ def main():
     ap.add_argument("--y-dtype", choices=("bf16", "f32"), default="bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-gdn", action="store_true", help="skip the GDN measurement")
+    ap.add_argument("--no-kda", action="store_true", help="skip the KDA measurement")
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--cpu-steps", type=int, default=80)
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
@@ -483,7 +489,7 @@ def main():
         copy_probe(dev)
         return
 
-    from workloads import GDN, LARGE_BATCH
+    from workloads import GDN, KDA, LARGE_BATCH
     wl = LARGE_BATCH
     y_dtype = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
     print(f"[bench] {wl.name}: layers={args.layers} steps={args.steps} warmup={args.warmup}",
@@ -510,6 +516,11 @@ def main():
     if not args.no_gdn:
         gdn = bench_gdn(GDN, args.layers, args.steps, args.warmup, dev)
         print(f"[bench] gdn done: {gdn['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
+              flush=True)
+    kda = None
+    if not args.no_kda:
+        kda = bench_gdn(KDA, args.layers, args.steps, args.warmup, dev)
+        print(f"[bench] kda done: {kda['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
               flush=True)
     spec = None
     if not args.no_gdn:
@@ -564,6 +575,7 @@ def main():
         },
         "speedup_vs_standard": m["replay_updates_per_s"] / m["standard_updates_per_s"],
         "gdn": gdn,
+        "kda": kda,
         "gdn_spec": spec,
         "stochastic_rounding": m.get("stochastic_rounding"),
         "tp8_share": tp,

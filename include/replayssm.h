@@ -192,7 +192,9 @@ int replayssm_ring_reset(const rssm_dims* dims, int32_t* write_pos,
 /*
  * GDN dimensions.  Supported: dk == dv == 128 (also 64); v_heads a multiple
  * of k_heads (value head hv reads key head hv / (v_heads / k_heads));
- * 1 <= ring_len <= 64 with 4*ring_len*(K+V) bytes within 64 KB; state_dtype RSSM_F32; io_dtype (q, k, v, k ring) and
+ * 1 <= ring_len <= 64 with the staged ring rows within 64 KB of LDS (about
+ * ring_len*(2K + 4V) bytes for bf16 q/k/v, plus 4*ring_len*K for the KDA gate
+ * rows; RSSM_ESHAPE otherwise); state_dtype RSSM_F32; io_dtype (q, k, v, k ring) and
  * out_dtype RSSM_F32 or RSSM_BF16.  scale <= 0 selects 1/sqrt(dk).
  */
 typedef struct rssm_gdn_dims {
@@ -236,6 +238,38 @@ int gdn_standard_decode(const rssm_gdn_dims* dims, void* state,
  *   Cursor and status rules as for replayssm_decode.
  */
 int replayssm_gdn_decode(const rssm_gdn_dims* dims, void* state, float* d_ring,
+                         void* k_ring, float* g_ring, const int32_t* slot_idx,
+                         const int32_t* write_pos, const uint8_t* is_flush,
+                         int32_t* next_write_pos, uint8_t* next_is_flush,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const float* beta, void* o,
+                         int32_t* status, hipStream_t stream);
+
+/*
+ * KDA: the gated delta rule with a per-key-channel gate g in R^K (sglang
+ * #28451: Implementation item 1 - one decode kernel serves the GDN scalar
+ * gate and the KDA per-K gate; review notes - the KDA ring holds a gate row
+ * per entry, g_cache [slots, HV, L, K]).  Same dims, layouts, cursor and
+ * status rules as the GDN calls, except that g is [batch, HV, K] float32
+ * [16B] and g_ring [num_slots, HV, L, K] float32 [16B].
+ *
+ * kda_standard_decode - the recurrence, per value head:
+ *     S = S diag(g);  S += beta * outer(v - S@k, k);  o = scale * S@q
+ *
+ * replayssm_kda_decode - ReplaySSM decode.  With Gamma = prod_{j<=w} g_j and
+ * gamma_i = prod_{i<j<=w} g_j taken per channel and kt_i = gamma_i * k_i:
+ *     pred = S0@(Gamma*k_w) + sum_{i<w} d_i*(kt_i . k_w)
+ *     d_w  = beta_w*(v_w - pred)
+ *     o    = scale*[S0@(Gamma*q) + sum_{i<=w} d_i*(kt_i . q)]
+ *   f == 0: (d_w, k_w, g_w) written at ring position w;
+ *   f != 0: state = S0 diag(Gamma) + sum_{i<=w} outer(d_i, kt_i).
+ */
+int kda_standard_decode(const rssm_gdn_dims* dims, void* state,
+                        const int32_t* slot_idx, const void* q, const void* k,
+                        const void* v, const float* g, const float* beta,
+                        void* o, int32_t* status, hipStream_t stream);
+
+int replayssm_kda_decode(const rssm_gdn_dims* dims, void* state, float* d_ring,
                          void* k_ring, float* g_ring, const int32_t* slot_idx,
                          const int32_t* write_pos, const uint8_t* is_flush,
                          int32_t* next_write_pos, uint8_t* next_is_flush,

@@ -20,7 +20,8 @@ import torch  # loads the HIP runtime the library then binds to
 __all__ = [
     "ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
     "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
-    "replayssm_gdn_spec_commit", "build_metadata",
+    "replayssm_gdn_spec_commit", "kda_standard_decode", "replayssm_kda_decode",
+    "build_metadata",
     "check_copy_sources", "library_path", "load",
     "RssmError", "ST_BAD_WRITE_POS", "ST_RING_OVERFLOW", "ST_BAD_SLOT",
     "ST_BAD_ROW", "EXPORTS",
@@ -32,7 +33,8 @@ F32, BF16 = 0, 1
 ST_BAD_WRITE_POS, ST_RING_OVERFLOW, ST_BAD_SLOT, ST_BAD_ROW = 1, 2, 4, 8
 EXPORTS = ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
            "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
-           "replayssm_gdn_spec_commit", "replayssm_build_metadata",
+           "replayssm_gdn_spec_commit", "kda_standard_decode", "replayssm_kda_decode",
+           "replayssm_build_metadata",
            "replayssm_check_copy_sources", "replayssm_strerror", "replayssm_abi_version")
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -86,9 +88,11 @@ def load():
     lib.replayssm_gdn_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 17
     lib.replayssm_gdn_spec_verify.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 16
     lib.replayssm_gdn_spec_commit.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 13
+    lib.kda_standard_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 10
+    lib.replayssm_kda_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 17
     for fn in ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
                "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
-               "replayssm_gdn_spec_commit"):
+               "replayssm_gdn_spec_commit", "kda_standard_decode", "replayssm_kda_decode"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.replayssm_build_metadata.argtypes = [I, I, I, P, P, P, P, P]
     lib.replayssm_build_metadata.restype = ctypes.c_int
@@ -303,7 +307,7 @@ def _gdn_dims(state, q, v, ring_len, o_dtype, scale):
                    0.0 if scale is None else float(scale))
 
 
-def _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev):
+def _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev, kda=False):
     ns, HV, V, K = state.shape
     _need(state, "state", torch.float32)
     _need(q, "q", (torch.float32, torch.bfloat16), dev=dev)
@@ -312,7 +316,7 @@ def _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev):
     _need(q, "q", io, (nb, HK, K))
     _need(k, "k", io, (nb, HK, K), dev=dev)
     _need(v, "v", io, (nb, HV, V), dev=dev)
-    _need(g, "g", torch.float32, (nb, HV), dev=dev)
+    _need(g, "g", torch.float32, (nb, HV, K) if kda else (nb, HV), dev=dev)
     _need(beta, "beta", torch.float32, (nb, HV), dev=dev)
     if o is None:
         o = torch.empty((nb, HV, V), dtype=out_dtype or io, device=dev)
@@ -320,19 +324,53 @@ def _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev):
     return nb, HK, o
 
 
-def gdn_standard_decode(state, slot_idx, q, k, v, g, beta, o=None, scale=None,
-                        status=None, out_dtype=None, stream=None):
-    """Recurrent gated-delta-rule step (reads and writes ``state``); returns o."""
+def _gated_standard(fn, kda, state, slot_idx, q, k, v, g, beta, o, scale, status,
+                    out_dtype, stream):
     dev = _need(state, "state").device
-    nb, HK, o = _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev)
+    nb, HK, o = _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev, kda)
     _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
     _opt(status, "status", torch.int32, (1,))
     d = _gdn_dims(state, q, v, 1, o.dtype, scale)
-    rc = load().gdn_standard_decode(
+    rc = getattr(load(), fn)(
         ctypes.byref(d), _ptr(state), _ptr(slot_idx), _ptr(q), _ptr(k), _ptr(v),
         _ptr(g), _ptr(beta), _ptr(o), _ptr(status), _stream(stream))
-    _check("gdn_standard_decode", rc)
+    _check(fn, rc)
     return o
+
+
+def _gated_replay(fn, kda, state, d_ring, k_ring, g_ring, slot_idx, write_pos, is_flush,
+                  q, k, v, g, beta, o, next_write_pos, next_is_flush, scale, status,
+                  out_dtype, stream):
+    dev = _need(state, "state").device
+    ns, HV, V, K = state.shape
+    nb, HK, o = _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev, kda)
+    _need(d_ring, "d_ring", torch.float32, dev=dev)
+    L = d_ring.shape[2]
+    _need(d_ring, "d_ring", torch.float32, (ns, HV, L, V))
+    _need(k_ring, "k_ring", q.dtype, (ns, HK, L, K), dev=dev)
+    _need(g_ring, "g_ring", torch.float32, (ns, HV, L, K) if kda else (ns, HV, L), dev=dev)
+    _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
+    _need(write_pos, "write_pos", torch.int32, (nb,), dev=dev)
+    _need(is_flush, "is_flush", torch.uint8, (nb,), dev=dev)
+    _opt(next_write_pos, "next_write_pos", torch.int32, (nb,), dev=dev)
+    _opt(next_is_flush, "next_is_flush", torch.uint8, (nb,), dev=dev)
+    _opt(status, "status", torch.int32, (1,))
+    d = _gdn_dims(state, q, v, L, o.dtype, scale)
+    rc = getattr(load(), fn)(
+        ctypes.byref(d), _ptr(state), _ptr(d_ring), _ptr(k_ring), _ptr(g_ring),
+        _ptr(slot_idx), _ptr(write_pos), _ptr(is_flush), _ptr(next_write_pos),
+        _ptr(next_is_flush), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(o), _ptr(status), _stream(stream))
+    _check(fn, rc)
+    return o
+
+
+def gdn_standard_decode(state, slot_idx, q, k, v, g, beta, o=None, scale=None,
+                        status=None, out_dtype=None, stream=None):
+    """Recurrent gated-delta-rule step (reads and writes ``state``); returns o.
+    g, beta [batch, HV] float32."""
+    return _gated_standard("gdn_standard_decode", False, state, slot_idx, q, k, v, g, beta,
+                           o, scale, status, out_dtype, stream)
 
 
 def replayssm_gdn_decode(state, d_ring, k_ring, g_ring, slot_idx, write_pos,
@@ -344,28 +382,31 @@ def replayssm_gdn_decode(state, d_ring, k_ring, g_ring, slot_idx, write_pos,
     Rings: d_ring [slots, HV, L, V] float32, k_ring [slots, HK, L, K] (io
     dtype), g_ring [slots, HV, L] float32.
     """
-    dev = _need(state, "state").device
-    ns, HV, V, K = state.shape
-    nb, HK, o = _gdn_inputs(state, q, k, v, g, beta, o, out_dtype, dev)
-    _need(d_ring, "d_ring", torch.float32, dev=dev)
-    L = d_ring.shape[2]
-    _need(d_ring, "d_ring", torch.float32, (ns, HV, L, V))
-    _need(k_ring, "k_ring", q.dtype, (ns, HK, L, K), dev=dev)
-    _need(g_ring, "g_ring", torch.float32, (ns, HV, L), dev=dev)
-    _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
-    _need(write_pos, "write_pos", torch.int32, (nb,), dev=dev)
-    _need(is_flush, "is_flush", torch.uint8, (nb,), dev=dev)
-    _opt(next_write_pos, "next_write_pos", torch.int32, (nb,), dev=dev)
-    _opt(next_is_flush, "next_is_flush", torch.uint8, (nb,), dev=dev)
-    _opt(status, "status", torch.int32, (1,))
-    d = _gdn_dims(state, q, v, L, o.dtype, scale)
-    rc = load().replayssm_gdn_decode(
-        ctypes.byref(d), _ptr(state), _ptr(d_ring), _ptr(k_ring), _ptr(g_ring),
-        _ptr(slot_idx), _ptr(write_pos), _ptr(is_flush), _ptr(next_write_pos),
-        _ptr(next_is_flush), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-        _ptr(o), _ptr(status), _stream(stream))
-    _check("replayssm_gdn_decode", rc)
-    return o
+    return _gated_replay("replayssm_gdn_decode", False, state, d_ring, k_ring, g_ring,
+                         slot_idx, write_pos, is_flush, q, k, v, g, beta, o, next_write_pos,
+                         next_is_flush, scale, status, out_dtype, stream)
+
+
+def kda_standard_decode(state, slot_idx, q, k, v, g, beta, o=None, scale=None,
+                        status=None, out_dtype=None, stream=None):
+    """Recurrent KDA step (per-key-channel gate g [batch, HV, K] float32);
+    reads and writes ``state``; returns o."""
+    return _gated_standard("kda_standard_decode", True, state, slot_idx, q, k, v, g, beta,
+                           o, scale, status, out_dtype, stream)
+
+
+def replayssm_kda_decode(state, d_ring, k_ring, g_ring, slot_idx, write_pos,
+                         is_flush, q, k, v, g, beta, o=None, next_write_pos=None,
+                         next_is_flush=None, scale=None, status=None,
+                         out_dtype=None, stream=None):
+    """One KDA ReplaySSM decode step; returns o.
+
+    g [batch, HV, K] float32; rings as for replayssm_gdn_decode except
+    g_ring [slots, HV, L, K] float32.
+    """
+    return _gated_replay("replayssm_kda_decode", True, state, d_ring, k_ring, g_ring,
+                         slot_idx, write_pos, is_flush, q, k, v, g, beta, o, next_write_pos,
+                         next_is_flush, scale, status, out_dtype, stream)
 
 
 def _spec_rings(state, d_ring, k_ring, g_ring, v_ring, beta_ring, io, dev):

@@ -1,6 +1,6 @@
-// Gated-delta-rule (GDN) decode kernels for gfx950: the recurrent update and
-// the ReplaySSM ring decode (checkpoint S0 + ring of (d, k, g), fold on flush
-// rows only).
+// Gated-delta-rule decode kernels for gfx950: the recurrent update and the
+// ReplaySSM ring decode (checkpoint S0 + ring of (d, k, g), fold on flush
+// rows only), for the GDN scalar gate and the KDA per-key-channel gate.
 //
 // Method: sglang #28451 (GDN/KDA ReplaySSM decode) - Motivation (GDN decode
 // reads and writes the full [HV, V, K] state every step and is bandwidth
@@ -8,7 +8,10 @@
 // the output from S0 plus the ring; the state is refreshed every L steps);
 // the ring contents d [L, V], k [L, K], g [L] per slot follow the memory-pool
 // snippet of sglang #28695 "[GDN] Support ReplaySSM Ring Spec-Verify".
-// Formulas: see the contract in replayssm.h.
+// One kernel serves both gates through a compile-time switch (sglang #28451,
+// Implementation item 1); the KDA ring keeps a [K] gate row per entry
+// (review notes of the same report).  Formulas: see the contract in
+// replayssm.h.
 //
 // Mapping (one workgroup per (row, value head) tile of the [V, K] fp32
 // state; LPR = K/4 adjacent lanes hold one state row):
@@ -26,6 +29,14 @@
 // The contractions are two matrix-vector products and, on flush rows, a
 // rank-(w+1) update with w+1 <= L: too thin for the matrix cores to pay,
 // and the kernel is bound by the state stream, so they run on the VALU.
+//
+// KDA (per-channel gate g_j in R^K): gamma_i and Gamma are vectors over the
+// key channels.  The gate rows go to LDS with the other ring rows; one
+// thread per channel walks the entries from w down to 0 and replaces gate
+// row i by kt_i = gamma_i * k_i in place, leaving Gamma_c.  Every scalar gate
+// factor of the GDN path then moves into kt_i (ring dots kt_i . k_w,
+// kt_i . q and the rank update) and into Gamma * k_w, Gamma * q (S0 dots and
+// the fold's diagonal scale).
 #include <math.h>
 
 #include "gdn_common.hpp"
@@ -59,31 +70,35 @@ struct GdnArgs {
   float scale;
 };
 
-// LDS: 16-byte chunks [q | v | k rows (8-row multiples) | d rows 0..L-1 (fp32)]
-template <typename IT, int V, int K>
+// LDS: 16-byte chunks [q | v | k rows (8-row multiples) | d rows 0..L-1 (fp32)
+// | KDA: gate rows (fp32, 8-row multiples)]
+template <typename IT, int V, int K, bool KDA = false>
 struct GdnStage {
   static constexpr int IV = Elt<IT>::kPer16;
   static constexpr int QV = K / IV;  // chunks per q / k row
   static constexpr int VV = V / IV;  // chunks per v row
   static constexpr int DV = V / 4;   // chunks per d row
+  static constexpr int GV = K / 4;   // chunks per KDA gate row
   static_assert(K % IV == 0 && V % IV == 0, "rows are whole chunks");
   static constexpr int oK = QV + VV;
   static constexpr int oD(int L) { return oK + ((L + 7) & ~7) * QV; }
-  static constexpr int chunks(int L) { return oD(L) + L * DV; }
+  static constexpr int oG(int L) { return oD(L) + L * DV; }
+  static constexpr int chunks(int L) { return oG(L) + (KDA ? ((L + 7) & ~7) * GV : 0); }
 };
 
-template <typename IT, typename OT, int V, int K, bool REPLAY>
+template <typename IT, typename OT, int V, int K, bool REPLAY, bool KDA>
 __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kernel(const GdnArgs a) {
   using GS = GdnShape<V, K, REPLAY>;
-  using SG = GdnStage<IT, V, K>;
+  using SG = GdnStage<IT, V, K, KDA>;
   constexpr int SV = GS::SV, LPR = GS::LPR, NT = GS::NT, ITEMS = GS::ITEMS, RPI = GS::RPI;
   constexpr int IC = GS::IC;
-  constexpr int QV = SG::QV, VV = SG::VV, DV = SG::DV;
+  constexpr int QV = SG::QV, VV = SG::VV, DV = SG::DV, GV = SG::GV;
   constexpr long kIo = sizeof(IT);
 
   extern __shared__ __attribute__((aligned(16))) char lds[];
   __shared__ __attribute__((aligned(16))) float cf_lds[2 * NT];  // per wave: ring weights
-  __shared__ float gm_lds[64];                                   // gamma_i
+  __shared__ float gm_lds[64];                                   // gamma_i (GDN)
+  __shared__ __attribute__((aligned(16))) float gk_lds[KDA ? K : 4];  // Gamma_c (KDA)
 
   const int L = REPLAY ? a.ring_len : 1;
   const int HV = a.v_heads;
@@ -139,9 +154,10 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
   const long qk_cur = ((long)b * a.k_heads + hk) * K;             // q, k[b, hk, :]
   const long kring0 = ((long)s * a.k_heads + hk) * (long)L * K;   // k_ring[s, hk, 0, :]
   const long dring0 = ((long)s * HV + hv) * (long)L * V;          // d_ring[s, hv, 0, :]
-  const long gring0 = ((long)s * HV + hv) * L;
+  const long gring0 = ((long)s * HV + hv) * L * (KDA ? K : 1);
   const int oK = SG::oK;
   const int oD = SG::oD(L);
+  const int oG = SG::oG(L);
   auto dma_span = [&](int c0, int n, const char* ring, int nring, const char* cur) {
     for (int j = wave * 64; j < n; j += NT) {
       const int u = j + lane;
@@ -162,12 +178,17 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
       const char* dg = (const char*)a.d_ring + dring0 * 4;
       dma_span(oD, w * DV, dg, w * DV, dg);
     }
+    if constexpr (KDA)  // gate rows 0..w-1 from the ring, row w the current gate
+      dma_span(oG, (w + 1) * GV, REPLAY ? (const char*)(a.g_ring + gring0) : nullptr,
+               REPLAY ? w * GV : 0, (const char*)(a.g + ((long)b * HV + hv) * K));
   }
-  const float gw = a.g[(long)b * HV + hv];
+  const float gw = KDA ? 1.f : a.g[(long)b * HV + hv];
   const float bw = a.beta[(long)b * HV + hv];
   float gl = 1.f;  // g of entry `lane` (1 past w: neutral in products)
-  if (REPLAY && lane < w) gl = a.g_ring[gring0 + lane];
-  if (lane == w) gl = gw;
+  if constexpr (!KDA) {
+    if (REPLAY && lane < w) gl = a.g_ring[gring0 + lane];
+    if (lane == w) gl = gw;
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
@@ -175,15 +196,58 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
   const char* Vs = lds + QV * 16;
   const char* Ks = lds + oK * 16;
   float* Ds = reinterpret_cast<float*>(lds + (long)oD * 16);
+  float* Gs = reinterpret_cast<float*>(lds + (long)oG * 16);  // KDA gate rows -> kt rows
 
   // ---- 2. gates: gamma_i = prod_{i<j<=w} g_j (lane i), Gamma = prod_{j<=w} g_j
-  const float gam = L <= 16 ? row16_suffix_product_exclusive(gl)
-                            : wave_suffix_product_exclusive(gl, lane);
-  const float Gam = lane_value(gl * gam, 0);
+  float gam = 1.f, Gam = 1.f;
+  if constexpr (KDA) {
+    // per channel c: kt_i[c] = gamma_i[c] * k_i[c] over gate row i, Gamma_c;
+    // the current gate row goes to the ring here when the row appends
+    for (int c = tid; c < K; c += NT) {
+      if (REPLAY && !f) a.g_ring[gring0 + (long)w * K + c] = Gs[w * K + c];
+      float gp = 1.f;
+      for (int i = w; i >= 0; --i) {
+        const float gi = Gs[i * K + c];
+        Gs[i * K + c] = gp * LdsRead<IT>::one(Ks + (long)i * QV * 16, c);
+        gp *= gi;
+      }
+      gk_lds[c] = gp;
+    }
+    __syncthreads();
+  } else {
+    gam = L <= 16 ? row16_suffix_product_exclusive(gl) : wave_suffix_product_exclusive(gl, lane);
+    Gam = lane_value(gl * gam, 0);
+  }
 
-  // ---- 3. ring dots kk_i = k_i . k_w, kq_i = k_i . q: 16 lanes per row i
+  // ---- 3. ring dots kk_i = k_i . k_w, kq_i = k_i . q (KDA: kt_i in place of
+  // k_i): 16 lanes per row i
   float kk = 0.f, kq = 0.f;
-  {
+  if constexpr (KDA) {
+    constexpr int EPL = K / 16;
+    const int q16 = lane & 15;
+    float kw[EPL], qq[EPL];
+    LdsRead<IT>::template seg<EPL>(Ks + (long)w * QV * 16, q16 * EPL, kw);
+    LdsRead<IT>::template seg<EPL>(Qs, q16 * EPL, qq);
+    for (int pass = 0; pass * 4 <= w; ++pass) {
+      const int i = pass * 4 + (lane >> 4);  // rows past w: unused values
+      float kt[EPL];
+      LdsRead<float>::template seg<EPL>(reinterpret_cast<const char*>(Gs + i * K), q16 * EPL, kt);
+      float a1 = 0.f, a2 = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        a1 = fmaf(kt[e], kw[e], a1);
+        a2 = fmaf(kt[e], qq[e], a2);
+      }
+      a1 = group_sum<16>(a1);
+      a2 = group_sum<16>(a2);
+      a1 = __shfl(a1, (lane & 3) * 16, 64);
+      a2 = __shfl(a2, (lane & 3) * 16, 64);
+      if ((lane >> 2) == pass) {
+        kk = a1;
+        kq = a2;
+      }
+    }
+  } else {
     constexpr int EPL = K / 16;
     const int q16 = lane & 15;
     SegDot<IT, EPL> kw, qq;
@@ -203,18 +267,26 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
       }
     }
   }
-  const float kqw = lane_value(kq, w);        // k_w . q
+  const float kqw = lane_value(kq, w);        // k_w . q (gamma_w = 1)
   float* cw = cf_lds + wave * 128;            // [gamma_i kk_i (i<w) | gamma_i kq_i (i<w)]
   cw[lane] = lane < w ? gam * kk : 0.f;
   cw[64 + lane] = lane < w ? gam * kq : 0.f;
   __builtin_amdgcn_wave_barrier();
 
-  // ---- 4. S0 . k_w and S0 . q per state row
+  // ---- 4. S0 . k_w and S0 . q per state row (KDA: S0 . (Gamma*k_w), S0 . (Gamma*q))
   const int c = tid % LPR;
   const int prow = tid / LPR;
-  float kseg[SV], qseg[SV];
+  float kseg[SV], qseg[SV], gseg[SV];
   LdsRead<IT>::template seg<SV>(Ks + (long)w * QV * 16, c * SV, kseg);
   LdsRead<IT>::template seg<SV>(Qs, c * SV, qseg);
+  if constexpr (KDA) {
+    LdsRead<float>::template seg<SV>(reinterpret_cast<const char*>(gk_lds), c * SV, gseg);
+#pragma unroll
+    for (int j = 0; j < SV; ++j) {
+      kseg[j] *= gseg[j];
+      qseg[j] *= gseg[j];
+    }
+  }
   float pk[ITEMS], pq[ITEMS];
 #pragma unroll
   for (int it = 0; it < ITEMS; ++it) {
@@ -261,7 +333,8 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
   __syncthreads();  // d_w of every row and the gamma_i are in LDS
 
   if (!f) {
-    // ---- 6a. append (d_w, k_w, g_w) at ring position w
+    // ---- 6a. append (d_w, k_w, g_w) at ring position w (a KDA gate row went
+    // out in step 2)
     if (wave == 0) {
       const bool k_writer = (hv % a.vpk) == 0;  // one writer per key head
       for (int k2 = lane; k2 < DV + QV; k2 += 64) {
@@ -274,15 +347,18 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
           st16(a.k_ring, (kring0 + (long)w * K) * kIo + cc * 16, v);
         }
       }
-      if (lane == 0) a.g_ring[gring0 + w] = gw;
+      if (!KDA && lane == 0) a.g_ring[gring0 + w] = gw;
     }
     return;
   }
 
   // ---- 6b. flush: S_new = Gamma*S0 + sum_{i<=w} outer(gamma_i d_i, k_i)
-  for (int e = tid; e < (w + 1) * V; e += NT) {
-    const int i = e / V;
-    Ds[e] *= gm_lds[i];
+  // (KDA: S0 diag(Gamma) + sum_{i<=w} outer(d_i, kt_i))
+  if constexpr (!KDA) {
+    for (int e = tid; e < (w + 1) * V; e += NT) {
+      const int i = e / V;
+      Ds[e] *= gm_lds[i];
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -294,7 +370,10 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
       for (int j = 0; j < SV; ++j) sf[q][j] = 0.f;
     for (int i = 0; i <= w; ++i) {
       float kv[SV];
-      LdsRead<IT>::template seg<SV>(Ks + (long)i * QV * 16, c * SV, kv);
+      if constexpr (KDA)
+        LdsRead<float>::template seg<SV>(reinterpret_cast<const char*>(Gs + i * K), c * SV, kv);
+      else
+        LdsRead<IT>::template seg<SV>(Ks + (long)i * QV * 16, c * SV, kv);
 #pragma unroll
       for (int q = 0; q < IC; ++q) {
         const float dv = Ds[i * V + (i0 + q) * RPI + prow];
@@ -307,39 +386,40 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
       float s0[SV];
       Elt<float>::unpack(sv[i0 + q], s0);
 #pragma unroll
-      for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(Gam, s0[j], sf[q][j]);
+      for (int j = 0; j < SV; ++j) sf[q][j] = fmaf(KDA ? gseg[j] : Gam, s0[j], sf[q][j]);
       st16_stream(tptr, (long)lane_off + (i0 + q) * NT * 16, Elt<float>::pack(sf[q]));
     }
   }
 }
 
-template <typename IT, typename OT, int V, int K, bool REPLAY>
+template <typename IT, typename OT, int V, int K, bool REPLAY, bool KDA>
 static int launch_gdn(const GdnArgs& a, int batch, hipStream_t stream) {
   using GS = GdnShape<V, K, REPLAY>;
   const int L = REPLAY ? a.ring_len : 1;  // L <= 64: one gate per lane of a wave
-  const size_t lds = (size_t)GdnStage<IT, V, K>::chunks(L) * 16;
-  const size_t fixed = (2 * GS::NT + 64) * sizeof(float);  // weight and gate arrays
+  const size_t lds = (size_t)GdnStage<IT, V, K, KDA>::chunks(L) * 16;
+  const size_t fixed = (2 * GS::NT + 64 + (KDA ? K : 4)) * sizeof(float);  // weights, gates
   if (lds + fixed > kMaxLds) return RSSM_ESHAPE;  // ring rows must fit one workgroup's LDS
-  return launch_kernel(reinterpret_cast<const void*>(&gdn_decode_kernel<IT, OT, V, K, REPLAY>),
-                       (unsigned)((long)batch * a.v_heads), GS::NT, lds, stream, a);
+  return launch_kernel(
+      reinterpret_cast<const void*>(&gdn_decode_kernel<IT, OT, V, K, REPLAY, KDA>),
+      (unsigned)((long)batch * a.v_heads), GS::NT, lds, stream, a);
 }
 
-template <bool REPLAY, typename IT, typename OT>
+template <bool REPLAY, bool KDA, typename IT, typename OT>
 static int gdn_dispatch_shape(const GdnArgs& a, const rssm_gdn_dims& d, hipStream_t s) {
-  if (d.dv == 128 && d.dk == 128) return launch_gdn<IT, OT, 128, 128, REPLAY>(a, d.batch, s);
-  if (d.dv == 64 && d.dk == 64) return launch_gdn<IT, OT, 64, 64, REPLAY>(a, d.batch, s);
-  if (d.dv == 128 && d.dk == 64) return launch_gdn<IT, OT, 128, 64, REPLAY>(a, d.batch, s);
-  if (d.dv == 64 && d.dk == 128) return launch_gdn<IT, OT, 64, 128, REPLAY>(a, d.batch, s);
+  if (d.dv == 128 && d.dk == 128) return launch_gdn<IT, OT, 128, 128, REPLAY, KDA>(a, d.batch, s);
+  if (d.dv == 64 && d.dk == 64) return launch_gdn<IT, OT, 64, 64, REPLAY, KDA>(a, d.batch, s);
+  if (d.dv == 128 && d.dk == 64) return launch_gdn<IT, OT, 128, 64, REPLAY, KDA>(a, d.batch, s);
+  if (d.dv == 64 && d.dk == 128) return launch_gdn<IT, OT, 64, 128, REPLAY, KDA>(a, d.batch, s);
   return RSSM_ESHAPE;
 }
 
-template <bool REPLAY>
+template <bool REPLAY, bool KDA>
 static int gdn_dispatch(const GdnArgs& a, const rssm_gdn_dims& d, hipStream_t s) {
   switch (d.io_dtype * 2 + d.out_dtype) {
-    case 0: return gdn_dispatch_shape<REPLAY, float, float>(a, d, s);
-    case 1: return gdn_dispatch_shape<REPLAY, float, bf16>(a, d, s);
-    case 2: return gdn_dispatch_shape<REPLAY, bf16, float>(a, d, s);
-    case 3: return gdn_dispatch_shape<REPLAY, bf16, bf16>(a, d, s);
+    case 0: return gdn_dispatch_shape<REPLAY, KDA, float, float>(a, d, s);
+    case 1: return gdn_dispatch_shape<REPLAY, KDA, float, bf16>(a, d, s);
+    case 2: return gdn_dispatch_shape<REPLAY, KDA, bf16, float>(a, d, s);
+    case 3: return gdn_dispatch_shape<REPLAY, KDA, bf16, bf16>(a, d, s);
   }
   return RSSM_EDTYPE;
 }
@@ -367,19 +447,16 @@ static GdnArgs gdn_args(const rssm_gdn_dims* d) {
   return a;
 }
 
-}  // namespace rssm
-
-using namespace rssm;
-
-extern "C" int gdn_standard_decode(const rssm_gdn_dims* dims, void* state, const int32_t* slot_idx,
-                                   const void* q, const void* k, const void* v, const float* g,
-                                   const float* beta, void* o, int32_t* status,
-                                   hipStream_t stream) {
+template <bool KDA>
+static int standard_entry(const rssm_gdn_dims* dims, void* state, const int32_t* slot_idx,
+                          const void* q, const void* k, const void* v, const float* g,
+                          const float* beta, void* o, int32_t* status, hipStream_t stream) {
   int rc = gdn_check(dims, false);
   if (rc) return rc;
   if (dims->batch == 0) return RSSM_OK;  // empty batch: nothing to read or write
   if (!state || !slot_idx || !q || !k || !v || !g || !beta || !o) return RSSM_EINVAL;
   if (!aligned16(state) || !aligned16(q) || !aligned16(k) || !aligned16(v)) return RSSM_EINVAL;
+  if (KDA && !aligned16(g)) return RSSM_EINVAL;
   GdnArgs a = gdn_args(dims);
   a.state = static_cast<float*>(state);
   a.slot_idx = slot_idx;
@@ -391,16 +468,15 @@ extern "C" int gdn_standard_decode(const rssm_gdn_dims* dims, void* state, const
   a.o = o;
   a.status = status;
   a.ring_len = 1;
-  return gdn_dispatch<false>(a, *dims, stream);
+  return gdn_dispatch<false, KDA>(a, *dims, stream);
 }
 
-extern "C" int replayssm_gdn_decode(const rssm_gdn_dims* dims, void* state, float* d_ring,
-                                    void* k_ring, float* g_ring, const int32_t* slot_idx,
-                                    const int32_t* write_pos, const uint8_t* is_flush,
-                                    int32_t* next_write_pos, uint8_t* next_is_flush,
-                                    const void* q, const void* k, const void* v, const float* g,
-                                    const float* beta, void* o, int32_t* status,
-                                    hipStream_t stream) {
+template <bool KDA>
+static int replay_entry(const rssm_gdn_dims* dims, void* state, float* d_ring, void* k_ring,
+                        float* g_ring, const int32_t* slot_idx, const int32_t* write_pos,
+                        const uint8_t* is_flush, int32_t* next_write_pos, uint8_t* next_is_flush,
+                        const void* q, const void* k, const void* v, const float* g,
+                        const float* beta, void* o, int32_t* status, hipStream_t stream) {
   int rc = gdn_check(dims, true);
   if (rc) return rc;
   if (dims->batch == 0) return RSSM_OK;  // empty batch: nothing to read or write
@@ -410,6 +486,7 @@ extern "C" int replayssm_gdn_decode(const rssm_gdn_dims* dims, void* state, floa
   if (!aligned16(state) || !aligned16(d_ring) || !aligned16(k_ring) || !aligned16(q) ||
       !aligned16(k) || !aligned16(v))
     return RSSM_EINVAL;
+  if (KDA && (!aligned16(g) || !aligned16(g_ring))) return RSSM_EINVAL;
   if ((const void*)next_write_pos == (const void*)write_pos && next_write_pos) return RSSM_EINVAL;
   if ((const void*)next_is_flush == (const void*)is_flush && next_is_flush) return RSSM_EINVAL;
   GdnArgs a = gdn_args(dims);
@@ -430,5 +507,45 @@ extern "C" int replayssm_gdn_decode(const rssm_gdn_dims* dims, void* state, floa
   a.o = o;
   a.status = status;
   a.ring_len = dims->ring_len;
-  return gdn_dispatch<true>(a, *dims, stream);
+  return gdn_dispatch<true, KDA>(a, *dims, stream);
+}
+
+}  // namespace rssm
+
+using namespace rssm;
+
+extern "C" int gdn_standard_decode(const rssm_gdn_dims* dims, void* state, const int32_t* slot_idx,
+                                   const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, void* o, int32_t* status,
+                                   hipStream_t stream) {
+  return standard_entry<false>(dims, state, slot_idx, q, k, v, g, beta, o, status, stream);
+}
+
+extern "C" int replayssm_gdn_decode(const rssm_gdn_dims* dims, void* state, float* d_ring,
+                                    void* k_ring, float* g_ring, const int32_t* slot_idx,
+                                    const int32_t* write_pos, const uint8_t* is_flush,
+                                    int32_t* next_write_pos, uint8_t* next_is_flush,
+                                    const void* q, const void* k, const void* v, const float* g,
+                                    const float* beta, void* o, int32_t* status,
+                                    hipStream_t stream) {
+  return replay_entry<false>(dims, state, d_ring, k_ring, g_ring, slot_idx, write_pos, is_flush,
+                             next_write_pos, next_is_flush, q, k, v, g, beta, o, status, stream);
+}
+
+extern "C" int kda_standard_decode(const rssm_gdn_dims* dims, void* state, const int32_t* slot_idx,
+                                   const void* q, const void* k, const void* v, const float* g,
+                                   const float* beta, void* o, int32_t* status,
+                                   hipStream_t stream) {
+  return standard_entry<true>(dims, state, slot_idx, q, k, v, g, beta, o, status, stream);
+}
+
+extern "C" int replayssm_kda_decode(const rssm_gdn_dims* dims, void* state, float* d_ring,
+                                    void* k_ring, float* g_ring, const int32_t* slot_idx,
+                                    const int32_t* write_pos, const uint8_t* is_flush,
+                                    int32_t* next_write_pos, uint8_t* next_is_flush,
+                                    const void* q, const void* k, const void* v, const float* g,
+                                    const float* beta, void* o, int32_t* status,
+                                    hipStream_t stream) {
+  return replay_entry<true>(dims, state, d_ring, k_ring, g_ring, slot_idx, write_pos, is_flush,
+                            next_write_pos, next_is_flush, q, k, v, g, beta, o, status, stream);
 }

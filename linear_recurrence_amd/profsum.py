@@ -51,10 +51,10 @@ def _rows(path):
 
 def _is_replay(name):
     """The REPLAY template argument of a kernel name: the sixth of
-    mamba2_decode_kernel<ST, IT, OT, P, N, REPLAY, SR, PER>, the last of
-    gdn_decode_kernel<IT, OT, V, K, REPLAY>."""
+    mamba2_decode_kernel<ST, IT, OT, P, N, REPLAY, SR, PER>, the fifth of
+    gdn_decode_kernel<IT, OT, V, K, REPLAY, KDA>."""
     args = [a.strip() for a in name[name.index("<") + 1:name.rindex(">(")].split(",")]
-    return (args[5] if "mamba2_decode_kernel" in name else args[-1]) == "true"
+    return (args[5] if "mamba2_decode_kernel" in name else args[4]) == "true"
 
 
 def _dispatch_kib(path, kernel, replay, last):

@@ -23,6 +23,7 @@ import torch
 
 import linear_recurrence_amd as R
 from oracle import gdn as OG
+from oracle import kda as OK
 from oracle import mamba2 as OM
 from workloads import TORCH_DTYPES, GdnInputs, Mamba2Inputs
 
@@ -267,6 +268,12 @@ def run_gdn(wl, sample, o_dtype=torch.float32, steps=None, standard=True,
     tol_state = Tol("rel", 2e-5) if fp32_path else Tol("abs", 1e-2)
     sample = sorted(set(int(r) for r in sample))
     k = len(sample)
+    kda = wl.kda
+    gshape = (K,) if kda else ()  # per-entry gate: a [K] row (KDA) or a scalar (GDN)
+    rep_fn = R.replayssm_kda_decode if kda else R.replayssm_gdn_decode
+    std_fn = R.kda_standard_decode if kda else R.gdn_standard_decode
+    rep_ref = OK.kda_replay_step if kda else OG.gdn_replay_step
+    std_ref = OK.kda_standard_step if kda else OG.gdn_standard_step
     slots = gen.slot_idx()
     slots_np = slots.numpy()
     pool = gen.state_pool(slots.tolist())
@@ -275,7 +282,7 @@ def run_gdn(wl, sample, o_dtype=torch.float32, steps=None, standard=True,
     del pool
     dr = torch.full((ns, HV, L, V), float("nan"), dtype=torch.float32, device=dev)
     kr = torch.full((ns, HK, L, K), float("nan"), dtype=io, device=dev)
-    gr = torch.full((ns, HV, L), float("nan"), dtype=torch.float32, device=dev)
+    gr = torch.full((ns, HV, L) + gshape, float("nan"), dtype=torch.float32, device=dev)
     wp = torch.zeros(nb, dtype=torch.int32, device=dev)
     fl = torch.full((nb,), 1 if L == 1 else 0, dtype=torch.uint8, device=dev)
     nwp, nfl = torch.empty_like(wp), torch.empty_like(fl)
@@ -285,7 +292,7 @@ def run_gdn(wl, sample, o_dtype=torch.float32, steps=None, standard=True,
     o_rec = o_pool.copy()
     o_dr = np.full((k, HV, L, V), np.nan)
     o_kr = np.full((k, HK, L, K), np.nan)
-    o_gr = np.full((k, HV, L), np.nan)
+    o_gr = np.full((k, HV, L) + gshape, np.nan)
     o_sl = np.arange(k)
     o_wp = np.zeros(k, np.int32)
     o_fl = np.full(k, 1 if L == 1 else 0, np.uint8)
@@ -299,23 +306,23 @@ def run_gdn(wl, sample, o_dtype=torch.float32, steps=None, standard=True,
         gi = {n: v.to(dev) for n, v in inp.items()}
         flushing = c_fl.astype(bool).copy()
         w_before = c_wp.copy()
-        o = R.replayssm_gdn_decode(st_r, dr, kr, gr, sl, wp, fl, gi["q"], gi["k"], gi["v"],
-                                   gi["g"], gi["beta"], next_write_pos=nwp,
-                                   next_is_flush=nfl, status=status, out_dtype=o_dtype)
+        o = rep_fn(st_r, dr, kr, gr, sl, wp, fl, gi["q"], gi["k"], gi["v"], gi["g"],
+                   gi["beta"], next_write_pos=nwp, next_is_flush=nfl, status=status,
+                   out_dtype=o_dtype)
         os_ = None
         if standard:
-            os_ = R.gdn_standard_decode(st_s, sl, gi["q"], gi["k"], gi["v"], gi["g"],
-                                        gi["beta"], status=status, out_dtype=o_dtype)
+            os_ = std_fn(st_s, sl, gi["q"], gi["k"], gi["v"], gi["g"], gi["beta"],
+                         status=status, out_dtype=o_dtype)
         wp, nwp = nwp, wp
         fl, nfl = nfl, fl
         ni = {n: v[samp_t].double().numpy() for n, v in inp.items()}
-        o_ref, o_wp, o_fl, ost = OG.gdn_replay_step(
+        o_ref, o_wp, o_fl, ost = rep_ref(
             o_pool, o_dr, o_kr, o_gr, o_sl, o_wp, o_fl, ni["q"], ni["k"], ni["v"],
             ni["g"], ni["beta"], state_dtype="f32")
         assert ost == 0
         if standard:
-            os_ref = OG.gdn_standard_step(o_rec, o_sl, ni["q"], ni["k"], ni["v"], ni["g"],
-                                          ni["beta"], state_dtype="f32")
+            os_ref = std_ref(o_rec, o_sl, ni["q"], ni["k"], ni["v"], ni["g"], ni["beta"],
+                             state_dtype="f32")
         c_wp, c_fl = OM.cursor_advance(c_wp, c_fl, L)
         if not compare:
             return

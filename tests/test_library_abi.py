@@ -24,7 +24,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for fn in ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
-               "gdn_standard_decode", "replayssm_gdn_decode"):
+               "gdn_standard_decode", "replayssm_gdn_decode", "kda_standard_decode",
+               "replayssm_kda_decode"):
         assert fn in names
 
 
@@ -85,6 +86,21 @@ def test_host_validation_rejects_bad_arguments_without_a_gpu():
                                          V(0x2000), None, None, None) == -1        # no accepted
     assert lib.replayssm_gdn_spec_commit(ctypes.byref(gd), 4, *cm, V(0x3000), V(0x1000), None,
                                          V(0x3000), None, None, None) == -1        # aliasing
+    # KDA: the gate rows are vector operands (16-byte alignment) and take LDS
+    # of their own (a 64-entry ring of 128x128 bf16 rows no longer fits)
+    P = V(0x1000)
+    kd = R.GdnDims(2, 2, 2, 128, 128, 64, 4, 0, 1, 1, 0.0)
+    assert lib.replayssm_kda_decode(ctypes.byref(kd), *[P] * 7, None, None,
+                                    *[P] * 6, None, None) == -4
+    kd = R.GdnDims(2, 2, 2, 128, 128, 16, 4, 0, 1, 1, 0.0)
+    assert lib.replayssm_kda_decode(ctypes.byref(kd), P, P, P, V(0x1004), *[P] * 3, None,
+                                    None, *[P] * 6, None, None) == -1   # misaligned g_ring
+    assert lib.replayssm_kda_decode(ctypes.byref(kd), *[P] * 7, None, None, P, P, P,
+                                    V(0x1004), P, P, None, None) == -1  # misaligned g
+    assert lib.kda_standard_decode(ctypes.byref(kd), P, P, P, P, P, V(0x1004), P, P,
+                                   None, None) == -1
+    kd = R.GdnDims(2, 2, 2, 128, 128, 16, 4, 1, 1, 1, 0.0)               # bf16 state
+    assert lib.kda_standard_decode(ctypes.byref(kd), *[P] * 8, None, None) == -2
     d = R.Dims(**good)
     assert lib.replayssm_ring_reset(ctypes.byref(d), None, None, None, 0, None, None) == 0
     assert lib.replayssm_ring_reset(ctypes.byref(d), None, None, None, -1, None, None) == -1

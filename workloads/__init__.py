@@ -12,7 +12,9 @@ Recipe (one workload per decode shape; values drawn with NumPy PCG64):
   softplus(dt_bias) is uniform on [1e-3, 1e-1]); initial state ~ N(0, 0.1)
   (standard deviation 0.1).
 * GDN: q, k = N(0, 1) rows normalised to unit L2 norm (in float64, before
-  rounding); v ~ N(0, 1); beta = sigmoid(N(0, 1)); g = exp(-softplus(N(0,1))).
+  rounding); v ~ N(0, 1); beta = sigmoid(N(0, 1)); g = exp(-softplus(N(0,1))),
+  one draw per (row, value head), or per (row, value head, key channel) for
+  the KDA gate.
 * Every draw is rounded to its storage dtype here (bf16 by round-to-nearest-
   even through ``torch.Tensor.to``); consumers read exactly those values.
 * Streams are independent and addressable: the stream for (tag, index) is
@@ -101,6 +103,7 @@ class GdnWorkload:
     state_dtype: str
     seed: int
     desync: bool = False
+    kda: bool = False  # per-key-channel gate g [batch, HV, K] instead of [batch, HV]
 
     def with_batch(self, batch, steps=None, num_slots=None, name=None):
         d = dict(self.__dict__)
@@ -125,6 +128,8 @@ GROUPED = Mamba2Workload("mamba2_grouped_b256_h128_g8", 256, 128, 64, 128, 8,
 GROUPED_RINGS = (1, 4, 8, 16)
 GDN = GdnWorkload("gdn_b256_hk16_hv32_k128_L16", 256, 16, 32, 128, 128, 16,
                   128, 512, "bf16", "f32", 1004)
+KDA = GdnWorkload("kda_b256_h32_k128_L16", 256, 32, 32, 128, 128, 16, 128, 512, "bf16",
+                  "f32", 1005, kda=True)
 
 ALL = (TINY, LAYER_2P7B, LARGE_BATCH, GROUPED, GDN)
 
@@ -279,7 +284,7 @@ class GdnInputs:
         k = unit((nb, wl.k_heads, wl.dk))
         v = r.standard_normal((nb, wl.v_heads, wl.dv), dtype=np.float32)
         beta = (1.0 / (1.0 + np.exp(-r.standard_normal((nb, wl.v_heads))))).astype(np.float32)
-        a = r.standard_normal((nb, wl.v_heads))
+        a = r.standard_normal((nb, wl.v_heads, wl.dk) if wl.kda else (nb, wl.v_heads))
         g = np.exp(-(np.maximum(a, 0) + np.log1p(np.exp(-np.abs(a))))).astype(np.float32)
         out = {"q": q, "k": k, "v": v, "beta": beta, "g": g}
         if rows is not None:
