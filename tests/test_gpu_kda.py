@@ -47,10 +47,10 @@ def test_kda_full_size_desynced_rows():
 
 
 @pytest.mark.parametrize("L,dk,dv", [(5, 128, 128), (17, 128, 128), (32, 128, 128),
-                                     (64, 64, 64)])
+                                     (48, 128, 128), (64, 64, 64)])
 def test_kda_long_rings(L, dk, dv):
     """Rings past 16 entries up to the longest whose gate rows still fit the
-    workgroup's LDS (32 at K = V = 128, 64 at K = V = 64)."""
+    workgroup's LDS with bf16 inputs (48 at K = V = 128, 64 at K = V = 64)."""
     wl = GdnWorkload(f"kda_L{L}_{dk}x{dv}", 3, 2, 4, dk, dv, L, 2 * L + 3, 6, "bf16", "f32",
                      4200 + L, desync=True, kda=True)
     run_gdn(wl, sample=range(3), check_every=max(1, L // 8))

@@ -87,11 +87,12 @@ def test_host_validation_rejects_bad_arguments_without_a_gpu():
     assert lib.replayssm_gdn_spec_commit(ctypes.byref(gd), 4, *cm, V(0x3000), V(0x1000), None,
                                          V(0x3000), None, None, None) == -1        # aliasing
     # KDA: the gate rows are vector operands (16-byte alignment) and take LDS
-    # of their own (a 64-entry ring of 128x128 bf16 rows no longer fits)
+    # of their own (at K = V = 128 a ring fits 48 entries with bf16 inputs)
     P = V(0x1000)
-    kd = R.GdnDims(2, 2, 2, 128, 128, 64, 4, 0, 1, 1, 0.0)
-    assert lib.replayssm_kda_decode(ctypes.byref(kd), *[P] * 7, None, None,
-                                    *[P] * 6, None, None) == -4
+    for L, io in ((49, 1), (41, 0), (64, 1)):  # past 48 (bf16) / 40 (fp32) entries
+        kd = R.GdnDims(2, 2, 2, 128, 128, L, 4, 0, io, 1, 0.0)
+        assert lib.replayssm_kda_decode(ctypes.byref(kd), *[P] * 7, None, None,
+                                        *[P] * 6, None, None) == -4
     kd = R.GdnDims(2, 2, 2, 128, 128, 16, 4, 0, 1, 1, 0.0)
     assert lib.replayssm_kda_decode(ctypes.byref(kd), P, P, P, V(0x1004), *[P] * 3, None,
                                     None, *[P] * 6, None, None) == -1   # misaligned g_ring
