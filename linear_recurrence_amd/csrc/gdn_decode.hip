@@ -103,20 +103,26 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
   const int L = REPLAY ? a.ring_len : 1;
   const int HV = a.v_heads;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int b = tile / HV;
-  const int hv = tile - b * HV;
-  const int hk = hv / a.vpk;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rank = tile / HV;  // row rank; replay visits flush rows first
+  const int hv = tile - rank * HV;
+  const int hk = hv / a.vpk;
 
-  const int s = a.slot_idx[b];
+  RowPick pick{rank, 0, 0, true};
+  if constexpr (REPLAY)
+    pick = flush_first_pick(rank, gridDim.x / HV, a.slot_idx, a.write_pos, a.is_flush, lane);
+  else
+    pick.s = a.slot_idx[rank];
+  const int b = pick.b;
+  const int s = pick.s;
   int w = 0;
   bool f = true;
   int st = 0;
   if (REPLAY) {
-    w = a.write_pos[b];
-    f = a.is_flush[b] != 0;
+    w = pick.w;
+    f = pick.f;
     if (w < 0 || w >= L) {
       st |= RSSM_ST_BAD_WRITE_POS;
       w = w < 0 ? 0 : L - 1;

@@ -126,6 +126,46 @@ __device__ static inline int xcd_tile(int bid, int nblocks) {
   return xcd * q + (xcd < r ? xcd : r) + local;
 }
 
+// Row metadata of a replay tile, its rows visited flush rows first.  Tiles of
+// flush rows (state read, fold, state write) take several times longer than
+// output-only tiles and are the only ones that write the state; within each
+// aligned group of 64 batch rows the flush rows take the lowest ranks, so they
+// are dispatched first (longest jobs first) and the state writes of a launch
+// are issued together instead of spread through its read stream.  The map
+// rank -> row is a bijection for any batch.  One round trip: every lane
+// loads one row's (slot, write_pos, is_flush) and the wave picks its row by
+// ballots; the result is uniform.
+struct RowPick {
+  int b, s, w;
+  bool f;
+};
+__device__ static inline RowPick flush_first_pick(int rank, int nb, const int32_t* slot_idx,
+                                                  const int32_t* write_pos,
+                                                  const uint8_t* is_flush, int lane) {
+  const int g0 = rank & ~63;
+  const int n = nb - g0 < 64 ? nb - g0 : 64;
+  const int rloc = rank - g0;  // < n
+  const bool valid = lane < n;
+  int sl = 0, wl = 0;
+  bool fl = false;
+  if (valid) {
+    sl = slot_idx[g0 + lane];
+    wl = write_pos[g0 + lane];
+    fl = is_flush[g0 + lane] != 0;
+  }
+  const uint64_t fm = __ballot(fl);
+  const uint64_t om = __ballot(valid && !fl);
+  const int nf = __popcll(fm);
+  const uint64_t m = rloc < nf ? fm : om;        // rows of the wanted kind
+  const int r = rloc < nf ? rloc : rloc - nf;  // < popcount(m): exactly one lane matches
+  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+  const uint64_t hit = __ballot(((m >> lane) & 1) && below == r);
+  const int j = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+  return {g0 + j, __builtin_amdgcn_readlane(sl, j), __builtin_amdgcn_readlane(wl, j),
+          ((fm >> j) & 1) != 0};
+}
+
 // Value of v held by lane `lane` (uniform index), broadcast to the wave.
 __device__ static inline float lane_value(float v, int lane) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));

@@ -43,6 +43,14 @@ def test_gdn_full_size_desynced_rows():
     run_gdn(wl, sample=[3, 77, 150, 222], standard=False)
 
 
+def test_gdn_flush_first_row_order_with_a_ragged_row_group():
+    """100 desynced rows (a 64-row group and a ragged one of 36): replay tiles
+    take each group's flush rows first; cursors of every row bit-exact."""
+    wl = GdnWorkload("gdn_b100_desync", 100, 16, 32, 128, 128, 16, 40, 256, "bf16", "f32",
+                     1007, desync=True)
+    run_gdn(wl, sample=[1, 63, 64, 99])
+
+
 @pytest.mark.parametrize("L", [5, 17, 32, 64])
 def test_gdn_long_rings(L):
     """Rings past one 16-lane row of gates (suffix products over the wave),

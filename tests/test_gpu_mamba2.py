@@ -103,6 +103,15 @@ def test_large_batch_full_size_bench_configuration():
     run_mamba2(LARGE_BATCH, sample=_large_batch_sample(), y_dtype=torch.bfloat16)
 
 
+def test_flush_first_row_order_with_a_ragged_row_group():
+    """Replay tiles visit the flush rows of each 64-row group first; 110 rows
+    (a full group and a ragged one of 46) with uniform start positions: every
+    row is still advanced exactly once per step (all cursors bit-exact) and
+    sampled rows on both sides of the group boundary match the oracle."""
+    wl = LARGE_BATCH.with_batch(110, steps=40, num_slots=256, name="mamba2_b110_desync")
+    run_mamba2(wl, sample=[0, 37, 63, 64, 90, 109], y_dtype=torch.float32)
+
+
 def test_large_batch_full_size_fp32_output():
     run_mamba2(LARGE_BATCH, sample=_large_batch_sample()[::3], y_dtype=torch.float32,
                standard=False)
