@@ -15,9 +15,10 @@
 //
 // Mapping (one workgroup per (row, value head) tile of the [V, K] fp32
 // state; LPR = K/4 adjacent lanes hold one state row):
-//  * every global read of the step is issued at once: the tile into
-//    registers with raw buffer loads, q, v, k_0..k_w and d_0..d_{w-1} into
-//    LDS with direct-to-LDS loads, the gates into lanes;
+//  * every global read of the step is issued at once: q, v, k_0..k_w and
+//    d_0..d_{w-1} into LDS with direct-to-LDS loads, the gates into lanes,
+//    then the tile into registers with raw buffer loads; the gate and ring
+//    work waits only for the staged rows, not for the tile;
 //  * gate products by DPP suffix scans, ring dots k_i.k_w and k_i.q on 16
 //    lanes each (packed bf16 dot2 for bf16 inputs), their weights broadcast
 //    through LDS;
@@ -149,13 +150,11 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
     return;
   }
 
-  // ---- 1. every global read of the step
+  // ---- 1. every global read of the step: staged rows and gates, then the tile
   char* const tptr = (char*)a.state + ((long)s * HV + hv) * (long)V * K * 4;
   const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(V * K * 4));
   const uint32_t lane_off = tid * 16;
   u32x4 sv[ITEMS];
-#pragma unroll
-  for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
 
   const long qk_cur = ((long)b * a.k_heads + hk) * K;             // q, k[b, hk, :]
   const long kring0 = ((long)s * a.k_heads + hk) * (long)L * K;   // k_ring[s, hk, 0, :]
@@ -193,10 +192,20 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
   float gl = 1.f;  // g of entry `lane` (1 past w: neutral in products)
   if constexpr (!KDA) {
     if (REPLAY && lane < w) gl = a.g_ring[gring0 + lane];
-    if (lane == w) gl = gw;
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  // the tile last: steps 2 and 3 need only the staged rows and the gates, so
+  // they run while the tile is still in flight (the scheduling barriers keep
+  // the issue order the counter wait below relies on)
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
+  static_assert(ITEMS < 64, "the vmcnt field holds 6 bits");
+  // everything but the ITEMS tile loads has landed: vmcnt <= ITEMS (bits 3:0
+  // and 15:14 of the immediate), expcnt and lgkmcnt 0
+  __builtin_amdgcn_s_waitcnt((ITEMS & 15) | ((ITEMS >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
+  if (!KDA && lane == w) gl = gw;
 
   const char* Qs = lds;
   const char* Vs = lds + QV * 16;

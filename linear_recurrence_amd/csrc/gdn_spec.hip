@@ -149,26 +149,11 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
     return;
   }
 
-  // ---- 1. every global read: the tile, then the staged rows, then gates
+  // ---- 1. every global read: the staged rows and gates, then the tile
   char* const tptr = (char*)a.state + ((long)s * HV + hv) * (long)V * K * 4;
   const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(V * K * 4));
   const uint32_t lane_off = tid * 16;
   u32x4 sv[ITEMS];
-  if constexpr (MF) {
-    // block (vb, kb): lane l takes S0[16*vb + l%16][32*kb + 8*(l/16) .. +8],
-    // the B operand layout of the 16x16x32 product
-    const uint32_t voff = (uint32_t)(((lane & 15) * K + 8 * (lane >> 4)) * 4);
-#pragma unroll
-    for (int jb = 0; jb < VM::NBLK; ++jb) {
-      const int vb = wave * VM::VBW + jb / VM::KB, kb = jb % VM::KB;
-      const uint32_t soff = (uint32_t)((16 * vb * K + 32 * kb) * 4);
-      sv[2 * jb] = bload16_nt(trs, voff, soff);
-      sv[2 * jb + 1] = bload16_nt(trs, voff, soff + 16);
-    }
-  } else {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
-  }
 
   const long kring0 = ((long)s * HK + hk) * (long)L * K;
   const long dring0 = ((long)s * HV + hv) * (long)L * V;
@@ -190,7 +175,30 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   if (lane < w) gl = a.g_ring[gring0 + lane];
   else if (lane < w + T) gl = a.g[(long)(b * T + (lane - w)) * HV + hv];
   const float bl = lane < T ? a.beta[(long)(b * T + lane) * HV + hv] : 0.f;
-  __builtin_amdgcn_s_waitcnt(0);
+  // the tile last: step 2 needs only the staged rows and the gates, so it
+  // runs while the tile is still in flight (the scheduling barriers keep the
+  // issue order the counter wait below relies on)
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MF) {
+    // block (vb, kb): lane l takes S0[16*vb + l%16][32*kb + 8*(l/16) .. +8],
+    // the B operand layout of the 16x16x32 product
+    const uint32_t voff = (uint32_t)(((lane & 15) * K + 8 * (lane >> 4)) * 4);
+#pragma unroll
+    for (int jb = 0; jb < VM::NBLK; ++jb) {
+      const int vb = wave * VM::VBW + jb / VM::KB, kb = jb % VM::KB;
+      const uint32_t soff = (uint32_t)((16 * vb * K + 32 * kb) * 4);
+      sv[2 * jb] = bload16_nt(trs, voff, soff);
+      sv[2 * jb + 1] = bload16_nt(trs, voff, soff + 16);
+    }
+  } else {
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
+  }
+  static_assert(ITEMS < 64, "the vmcnt field holds 6 bits");
+  // everything but the ITEMS tile loads has landed: vmcnt <= ITEMS (bits 3:0
+  // and 15:14 of the immediate), expcnt and lgkmcnt 0
+  __builtin_amdgcn_s_waitcnt((ITEMS & 15) | ((ITEMS >> 4) << 14));
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
   const char* Qs = lds;
@@ -408,8 +416,8 @@ struct CommitStage {
 };
 
 template <typename IT, int V, int K>
-__global__ void __launch_bounds__((GdnShape<V, K, false>::NT)) gdn_spec_commit_kernel(const SpecArgs a) {
-  using GS = GdnShape<V, K, false>;
+__global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_kernel(const SpecArgs a) {
+  using GS = GdnShape<V, K, true>;  // 256 threads: half the waves of the 512-thread shape
   using SG = CommitStage<IT, V, K>;
   constexpr int SV = GS::SV, LPR = GS::LPR, NT = GS::NT, ITEMS = GS::ITEMS, RPI = GS::RPI;
   constexpr int QV = SG::QV, VV = SG::VV;
@@ -532,7 +540,7 @@ static int launch_commit(const SpecArgs& a, int batch, hipStream_t stream) {
   const size_t lds = CommitStage<IT, V, K>::bytes(a.ring_len);
   if (lds > kMaxLds) return RSSM_ESHAPE;
   return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_commit_kernel<IT, V, K>),
-                       (unsigned)((long)batch * a.v_heads), GdnShape<V, K, false>::NT, lds, stream,
+                       (unsigned)((long)batch * a.v_heads), GdnShape<V, K, true>::NT, lds, stream,
                        a);
 }
 
