@@ -17,9 +17,9 @@ share of the layer (10 of 80 heads); the GDN replay/standard decode at
 batch 256 (16 key / 32 value heads, K = V = 128, L = 16, bf16 q/k/v, fp32
 state) and its speculative verify + commit with 4 drafts per round; the KDA
 (per-key-channel gate) replay/standard decode at batch 256, 32 heads,
-K = V = 128, L = 16; the host
-metadata builder; and the float64 CPU oracle on a bounded
-sample (``cpu_baseline``).
+K = V = 128, L = 16; the host metadata builder; and the float64 CPU oracle
+on a bounded sample, on one thread (``cpu_baseline``) and sharded by rows
+over up to 16 processes (``cpu_baseline_parallel``).
 
 Roofline: algorithmic bytes per launch (checkpoint reads, ring reads of the
 live entries, ring appends, flush write-backs, step inputs, outputs and
@@ -368,42 +368,89 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev):
     return res
 
 
-def cpu_baseline(wl, rows, steps):
-    """The float64 oracle's replay step on a bounded sample of the workload:
-    `rows` rows of the batch for `steps` steps from its first (desync) warm-up
-    step, single-threaded; inputs drawn before the clock starts."""
+def _oracle_sample(wl, r0, r1, steps):
+    """The float64 oracle's replay steps for batch rows [r0, r1) over `steps`
+    steps from the workload's first (desync) warm-up step: inputs are drawn
+    here, the returned function runs the steps (single-threaded) and returns
+    its start and end times."""
     from threadpoolctl import threadpool_limits
 
     from oracle import mamba2 as OM
     from workloads import Mamba2Inputs
     gen = Mamba2Inputs(wl)
     H, P, N, G, L = wl.nheads, wl.headdim, wl.dstate, wl.ngroups, wl.ring_len
-    slots = gen.slot_idx().numpy()[:rows]
+    rows = r1 - r0
+    slots = gen.slot_idx().numpy()[r0:r1]
     pool = np.stack([gen.slot_state(int(s)).double().numpy() for s in slots])
     prm = {n: v.double().numpy() for n, v in gen.params().items()}
     xr = np.full((rows, H, L, P), np.nan)
     dr = np.full((rows, H, L), np.nan)
     br = np.full((rows, G, L, N), np.nan)
-    wp = np.zeros(rows, np.int32)
-    fl = np.zeros(rows, np.uint8)
     seq = []
     for t in range(steps):
         src = gen.warm_step(t) if t < L else gen.step(t - L)
-        force = gen.warm_force_flush(t).numpy()[:rows] if t < L else np.zeros(rows, np.uint8)
-        seq.append(({n: v[:rows].double().numpy() for n, v in src.items()}, force))
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        for inp, force in seq:
-            fl = fl | force
-            _, wp, fl, _ = OM.replay_step(pool, xr, dr, br, np.arange(rows), wp, fl, inp["x"],
-                                          inp["dt"], prm["A"], inp["B"], inp["C"], D=prm["D"],
-                                          z=inp["z"], dt_bias=prm["dt_bias"],
-                                          state_dtype=wl.state_dtype)
-        dt = time.perf_counter() - t0
+        force = gen.warm_force_flush(t).numpy()[r0:r1] if t < L else np.zeros(rows, np.uint8)
+        seq.append(({n: v[r0:r1].double().numpy() for n, v in src.items()}, force))
+
+    def run():
+        wp = np.zeros(rows, np.int32)
+        fl = np.zeros(rows, np.uint8)
+        with threadpool_limits(1):
+            t0 = time.perf_counter()
+            for inp, force in seq:
+                fl = fl | force
+                _, wp, fl, _ = OM.replay_step(pool, xr, dr, br, np.arange(rows), wp, fl,
+                                              inp["x"], inp["dt"], prm["A"], inp["B"], inp["C"],
+                                              D=prm["D"], z=inp["z"], dt_bias=prm["dt_bias"],
+                                              state_dtype=wl.state_dtype)
+            return t0, time.perf_counter()
+    return run
+
+
+def cpu_baseline(wl, rows, steps):
+    """The float64 oracle's replay step on a bounded sample of the workload:
+    `rows` rows of the batch for `steps` steps, one thread; inputs drawn
+    before the clock starts."""
+    t0, t1 = _oracle_sample(wl, 0, rows, steps)()
+    dt = t1 - t0
     return {"value": rows * steps / dt, "unit": "state-updates/s", "cores": 1,
             "kind": "oracle",
             "sample": f"float64 NumPy replay oracle, {rows} of {wl.batch} rows x {steps} "
-                      f"steps ({L} desync warm-up steps first), one thread, {dt:.1f} s"}
+                      f"steps ({wl.ring_len} desync warm-up steps first), one thread, {dt:.1f} s"}
+
+
+_SHARD_BARRIER = None
+
+
+def _shard_init(barrier):
+    global _SHARD_BARRIER
+    _SHARD_BARRIER = barrier
+
+
+def _shard_run(job):
+    wl, r0, r1, steps = job
+    run = _oracle_sample(wl, r0, r1, steps)
+    _SHARD_BARRIER.wait()  # every shard has its inputs: start together
+    return run()
+
+
+def cpu_baseline_parallel(wl, rows_per_worker, steps, workers):
+    """The same oracle sharded by rows over `workers` fresh processes (one
+    thread each; each draws its rows' inputs, then all start together); rate =
+    all row-steps / (last end - first start).  Called before this process
+    initialises the GPU."""
+    import multiprocessing as mp
+    ctx = mp.get_context("spawn")
+    nrows = min(wl.batch, rows_per_worker * workers)
+    bounds = np.linspace(0, nrows, workers + 1).astype(int)
+    jobs = [(wl, int(bounds[i]), int(bounds[i + 1]), steps) for i in range(workers)]
+    with ctx.Pool(workers, initializer=_shard_init, initargs=(ctx.Barrier(workers),)) as pool:
+        spans = pool.map(_shard_run, jobs, chunksize=1)
+    dt = max(e for _, e in spans) - min(s for s, _ in spans)
+    return {"value": nrows * steps / dt, "unit": "state-updates/s", "cores": workers,
+            "kind": "oracle",
+            "sample": f"float64 NumPy replay oracle, rows 0..{nrows - 1} of {wl.batch} x {steps} "
+                      f"steps, {workers} processes of one thread, {dt:.1f} s"}
 
 
 def metadata_rate(rows, L, calls=2000):
@@ -479,9 +526,20 @@ def main():
               "(rows and heads shard with zero communication), so only --gpus 1 is "
               "supported.", file=sys.stderr)
         sys.exit(2)
-    if not torch.cuda.is_available():
+    if torch.cuda.device_count() < 1:  # counts devices without initialising them
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    from workloads import GDN, KDA, LARGE_BATCH
+    cpu = cpu_par = None
+    if not args.no_cpu and not args.copy_probe:
+        # CPU legs first: the parallel one forks, which must happen before
+        # this process initialises the GPU
+        cpu = cpu_baseline(LARGE_BATCH, args.cpu_rows, args.cpu_steps)
+        print(f"[bench] cpu oracle done: {cpu['sample']}", file=sys.stderr, flush=True)
+        workers = min(16, len(os.sched_getaffinity(0)))
+        cpu_par = cpu_baseline_parallel(LARGE_BATCH, 32, args.cpu_steps, workers)
+        print(f"[bench] parallel cpu oracle done: {cpu_par['sample']}", file=sys.stderr,
+              flush=True)
     import linear_recurrence_amd as R
     R.load()
     dev = torch.device("cuda:0")
@@ -489,7 +547,6 @@ def main():
         copy_probe(dev)
         return
 
-    from workloads import GDN, KDA, LARGE_BATCH
     wl = LARGE_BATCH
     y_dtype = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
     print(f"[bench] {wl.name}: layers={args.layers} steps={args.steps} warmup={args.warmup}",
@@ -526,10 +583,6 @@ def main():
     if not args.no_gdn:
         spec = bench_gdn_spec(GDN, 4, args.layers, 256, 16, dev)
         print(f"[bench] gdn spec done: {spec['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
-    cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(wl, args.cpu_rows, args.cpu_steps)
-        print(f"[bench] cpu oracle done: {cpu['sample']}", file=sys.stderr, flush=True)
 
     ms_per_step = m["replay_s"] / args.steps * 1e3
     achieved = m["replay_bytes_per_launch"] / (m["replay_s"] / args.steps) / 1e9
@@ -565,6 +618,7 @@ def main():
             "algorithmic_bytes_per_launch": m["replay_bytes_per_launch"],
         },
         "cpu_baseline": cpu,
+        "cpu_baseline_parallel": cpu_par,
         "standard": {
             "kernel": "ssu_standard_decode",
             "state_updates_per_s": m["standard_updates_per_s"],
