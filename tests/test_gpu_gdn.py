@@ -58,3 +58,11 @@ def test_gdn_long_rings(L):
     wl = GdnWorkload(f"gdn_L{L}", 3, 2, 4, 128, 128, L, 2 * L + 3, 6, "bf16", "f32",
                      3200 + L, desync=True)
     run_gdn(wl, sample=range(3), check_every=max(1, L // 8))
+
+
+def test_gdn_longest_fp32_ring():
+    """fp32 q/k/v rows take twice the LDS: 57 entries is the longest ring that
+    fits at K = V = 128."""
+    wl = GdnWorkload("gdn_L57_f32", 3, 2, 4, 128, 128, 57, 2 * 57 + 3, 6, "f32", "f32", 3300,
+                     desync=True)
+    run_gdn(wl, sample=range(3), check_every=8)

@@ -54,3 +54,11 @@ def test_kda_long_rings(L, dk, dv):
     wl = GdnWorkload(f"kda_L{L}_{dk}x{dv}", 3, 2, 4, dk, dv, L, 2 * L + 3, 6, "bf16", "f32",
                      4200 + L, desync=True, kda=True)
     run_gdn(wl, sample=range(3), check_every=max(1, L // 8))
+
+
+def test_kda_longest_fp32_ring():
+    """fp32 q/k/v rows and the gate rows: 40 entries is the longest ring that
+    fits at K = V = 128."""
+    wl = GdnWorkload("kda_L40_f32", 3, 2, 4, 128, 128, 40, 2 * 40 + 3, 6, "f32", "f32", 4300,
+                     desync=True, kda=True)
+    run_gdn(wl, sample=range(3), check_every=5)

@@ -83,6 +83,19 @@ def test_every_tile_shape_on_a_full_grid(P, N):
     run_mamba2(wl, sample=[0, nb // 2, nb - 1], standard=False)
 
 
+@pytest.mark.parametrize("L,P,N,io,state_dt", [
+    (17, 32, 64, "bf16", "f32"), (32, 64, 128, "f32", "f32"), (64, 64, 128, "bf16", "bf16"),
+    (64, 64, 128, "f32", "f32")])
+def test_long_rings_up_to_the_maximum(L, P, N, io, state_dt):
+    """Rings past one 16-lane row of dt (the wave-wide suffix scan and the
+    ring-term loop past 16 entries) up to the 64-entry maximum; start positions
+    uniform, so every write position and a flush of every row occur."""
+    print(f"case: long ring L={L} P={P} N={N} io={io} state={state_dt}", flush=True)
+    wl = Mamba2Workload(f"ring_L{L}_p{P}_n{N}_{io}", 4, 6, P, N, 2, L, 2 * L + 3, 8, io,
+                        state_dt, 2300 + L, desync=True)
+    run_mamba2(wl, sample=range(4), check_every=max(1, L // 8))
+
+
 def test_layer_2p7b_full_size():
     """64 rows, 80 heads, dstate 128, L=16, bf16 io, fp32 pool of 1024 slots,
     256 steps; every row's cursors checked, 8 rows against the oracle."""
