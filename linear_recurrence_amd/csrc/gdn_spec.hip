@@ -12,17 +12,18 @@
 // closed-form fold drifted on long outputs, the exact fold restored parity).
 // Formulas: see the contract in replayssm.h.
 //
-// Verify mapping: one workgroup per (row, value head) fp32 [V, K] tile, the
-// tile read once into registers; q, v of the T drafts, the k rows of the
-// committed entries and of the drafts, and the committed d rows staged in
-// LDS by direct-to-LDS loads.  The waves form, per draft t at ring position
-// p = w + t (one draft per wave at a time), the gate products (DPP suffix
-// products over the lanes holding g_0..g_p) and the weighted dots
-// gamma_i*(k_i.k_p), gamma_i*(k_i.q_t);
-// every lane forms S0.k_p and S0.q_t for its state rows (2T butterfly row
-// reductions) and then walks the drafts in order, keeping the new d values
-// of its rows in registers.  The drafts' (d, k, g, v, beta) are written to
-// ring entries w..w+T-1; the state and the cursor are not touched.
+// Verify mapping: one workgroup per (row, value head) fp32 [V, K] tile.  q, v
+// of the T drafts, the k rows of the committed entries and of the drafts,
+// and the committed d rows are staged in LDS by direct-to-LDS loads, then
+// the tile is read once into registers.  While the tile is in flight the
+// waves form, per draft t at ring position p = w + t (one draft per wave at
+// a time), the gate products (DPP suffix products over the lanes holding
+// g_0..g_p) and the weighted dots gamma_i*(k_i.k_p), gamma_i*(k_i.q_t).
+// Then S0.k_p and S0.q_t for every state row (with bf16 inputs one matrix-core
+// product per wave, otherwise 2T butterfly row reductions), and each state
+// row walks the drafts in order, keeping the new d values in registers.
+// The drafts' (d, k, g, v, beta) are written to ring entries w..w+T-1; the
+// state and the cursor are not touched.
 //
 // Commit mapping: one workgroup per (row, value head); rows that do not
 // flush only advance the cursor.  Flushing tiles hold the state in fp32

@@ -13,18 +13,20 @@
 // Mapping: one workgroup per (row, head) tile of the [P, N] state, sized so
 // that every lane streams 16 vectors of 16 bytes (a 16 KB bf16 tile is one
 // wave).  The work is one memory round trip followed by arithmetic:
-//  * row metadata arrives through scalar loads; then every global read of
+//  * row metadata in one round trip (replay: the tile's rank picks a row,
+//    the flush rows of each 64-row group first); then every global read of
 //    the step is issued at once: the tile into registers (non-temporal), and
 //    C, z and the w+1 ring rows of x and B straight into LDS with
 //    global_load_lds (no registers, no conversion pass), and dt;
-//  * decay weights come from a wave-wide suffix scan of dt; B_i.C from
-//    16-lane dot products; both stay in lanes and are broadcast with
-//    readlane, so there are no serial LDS loops;
+//  * decay weights come from a suffix scan of dt across lanes (DPP within a
+//    16-lane row, shuffles past 16 entries); B_i.C from 8-lane dot products;
+//    the per-entry weights stay in lanes (readlane in the fold) or go
+//    through a 64-float LDS array (output rows);
 //  * LPR = N / (elements per vector) adjacent lanes hold one state row; a
 //    butterfly transpose leaves each lane with whole row sums;
 //  * the flush branch depends only on the row, so it is uniform across the
-//    workgroup: flush tiles fold the ring into their registers and store the
-//    new state, the others only read;
+//    workgroup: flush tiles fold the ring into their registers in
+//    double-buffered chunks and store the new state, the others only read;
 //  * blockIdx is remapped so each XCD works on a contiguous range of rows.
 #pragma once
 
