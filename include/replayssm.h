@@ -4,7 +4,9 @@
  * One decode step of a Mamba2 selective state update for a batch of rows,
  * either the standard read+write update or the ReplaySSM output-only form
  * (a checkpoint S0 plus a per-slot ring of the last inputs, folded into the
- * state only on flush rows), plus the gated-delta-rule (GDN) counterparts.
+ * state only on flush rows), plus the gated-delta-rule counterparts (GDN
+ * with a scalar gate, KDA with a per-key-channel gate), GDN speculative
+ * verify and commit from the ring, and host-side cursor helpers.
  *
  * Sources (page title, then section):
  *  - vLLM #48018 "[Kernel] ReplaySSM: cache SSM inputs for faster Mamba2
@@ -13,10 +15,12 @@
  *    is_flush branch; x/dt/B ring caches; per-row write_pos and is_flush
  *    from the metadata builder), key source snippet of mamba_mixer2.py (the
  *    argument lists of the replay op and of the baseline update).
- *  - sglang #28451 (GDN/KDA ReplaySSM decode): Motivation and Implementation
- *    items 1-3 (GDN ring decode, static cursor buffers, copy rules).
+ *  - sglang #28451 (GDN/KDA ReplaySSM decode): Motivation, Implementation
+ *    items 1-3 (one ring decode kernel for the GDN and KDA gates, static
+ *    cursor buffers, copy rules) and review notes (the KDA gate ring).
  *  - sglang #28695 "[GDN] Support ReplaySSM Ring Spec-Verify": memory-pool
- *    snippet (the GDN ring holds d [L,V], k [L,K], g [L] per slot).
+ *    snippet (the GDN ring holds d [L,V], k [L,K], g [L] per slot) and
+ *    Implementation items 2-4 (spec verify from the ring, exact fold).
  *  - vLLM #52506 "[Mamba] Add FlashInfer ReplaySSM backend": Implementation
  *    item 1 (ring cursors are reset when a slot is reused).
  *
@@ -31,9 +35,10 @@
  *    Pointers accessed with 16-byte vector loads (marked [16B]) must be
  *    16-byte aligned.
  *  - Element types follow the *_dtype fields (RSSM_F32 = float, RSSM_BF16 =
- *    bfloat16 bit pattern).  A, D, dt_bias, dt_ring, the GDN d/g rings, g and
- *    beta are always float32.  bf16 stores round to nearest even from the
- *    fp32 value; all arithmetic is fp32.
+ *    bfloat16 bit pattern).  A, D, dt_bias, dt_ring, the GDN/KDA d and g
+ *    rings, g and beta are always float32.  bf16 stores round to nearest
+ *    even from the fp32 value (or stochastically, where rssm_dims.rounding
+ *    asks for it); all arithmetic is fp32.
  *  - Return value: RSSM_OK (0) or a negative RSSM_E* code (nothing is
  *    enqueued on an error other than RSSM_ELAUNCH).  No exception crosses
  *    the ABI.
