@@ -28,8 +28,8 @@
 // Commit mapping: one workgroup per (row, value head); rows that do not
 // flush only advance the cursor.  Flushing tiles hold the state in fp32
 // registers and apply the recurrence entry by entry (scale by g, row dots
-// with k by butterfly reduction, d shared through LDS, rank-1 update), then
-// store it.
+// with k by butterfly reduction, d passed within the wave through LDS,
+// rank-1 update; the waves never wait for one another), then store it.
 #include <math.h>
 
 #include "gdn_common.hpp"
@@ -501,7 +501,10 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_ke
       const int vr = RR::item(j, tid) * RPI + prow;
       if (writer) db[vr] = bi * (LdsRead<IT>::one(Vs + (long)i * VV * 16, vr) - part[j]);
     }
-    __syncthreads();  // d of entry i; the other buffer is free for entry i+1
+    // the d values of a wave's state rows come from that wave's own lanes
+    // (a row's lanes never span two waves) and one wave's LDS operations
+    // complete in order, so no workgroup barrier is needed here
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int it = 0; it < ITEMS; ++it) {
       const float dv = db[it * RPI + prow];
