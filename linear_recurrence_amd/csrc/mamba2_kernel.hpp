@@ -290,6 +290,67 @@ __device__ __forceinline__ void fold_from(u32x4 (&ra)[IC], u32x4 (&rb)[IC], floa
   }
 }
 
+// Ring appends of head hh for every row of the 64-row group starting at g0
+// (n rows): x[b, hh, :] and the step's dt go to ring position w of the row's
+// slot, and B[b, g, :] too when hh is the first head of its group g.  A row
+// appends only when it will not flush: is_flush = 0, 0 <= w <= L-2 and a
+// slot in range, the rule the row's own tiles apply.  The tiles of each
+// group's first row run this before their own work, so the launch issues its
+// ring writes together near its start instead of one small write per tile
+// spread through the read stream, where each costs far more than its bytes.
+template <typename IT, int P, int N, int NT>
+__device__ __forceinline__ void group_appends(const Mamba2Args& a, int g0, int n, int hh, int L,
+                                              int tid) {
+  constexpr int XV = P / Elt<IT>::kPer16, BV = N / Elt<IT>::kPer16;
+  constexpr int DEPTH = 8;  // vectors in flight per thread
+  constexpr long kIo = sizeof(IT);
+  const int lane = tid & 63;
+  const int H = a.nheads;
+  int sl = 0, wl = 0;
+  bool app = false;
+  if (lane < n) {
+    sl = a.slot_idx[g0 + lane];
+    wl = a.write_pos[g0 + lane];
+    app = a.is_flush[g0 + lane] == 0 && wl >= 0 && wl <= L - 2 && sl >= 0 && sl < a.num_slots;
+  }
+  const uint64_t am = __ballot(app);  // every wave holds the whole group
+  // copy rows of RV vectors: vector v of the batch is (row v / RV, chunk v % RV)
+  auto copy_rows = [&](int RV, const char* src, long src_row, long src_off, char* dst,
+                       long slot_mul, long dst_off, long row_bytes) {
+    for (int v0 = 0; v0 < 64 * RV; v0 += NT * DEPTH) {
+      u32x4 buf[DEPTH];
+      long dofs[DEPTH];
+      bool on[DEPTH];
+#pragma unroll
+      for (int q = 0; q < DEPTH; ++q) {
+        const int v = v0 + q * NT + tid;
+        const int r = (v / RV) & 63;
+        const int sr = __shfl(sl, r, 64);
+        const int wr = __shfl(wl, r, 64);
+        on[q] = v < 64 * RV && ((am >> r) & 1);
+        dofs[q] = ((long)sr * slot_mul + dst_off + wr) * row_bytes + (long)(v % RV) * 16;
+        if (on[q]) buf[q] = ld16(src, (long)(g0 + r) * src_row + src_off + (long)(v % RV) * 16);
+      }
+#pragma unroll
+      for (int q = 0; q < DEPTH; ++q)
+        if (on[q]) st16(dst, dofs[q], buf[q]);
+    }
+  };
+  // x_ring[s, hh, w, :] <- x[b, hh, :]
+  copy_rows(XV, (const char*)a.x, (long)H * P * kIo, (long)hh * P * kIo, (char*)a.x_ring,
+            (long)H * L, (long)hh * L, P * kIo);
+  if (hh % a.hpg == 0) {
+    // B_ring[s, g, w, :] <- B[b, g, :]
+    const int gg = hh / a.hpg;
+    copy_rows(BV, (const char*)a.B, (long)a.ngroups * N * kIo, (long)gg * N * kIo,
+              (char*)a.B_ring, (long)a.ngroups * L, (long)gg * L, N * kIo);
+  }
+  if (tid < 64 && app) {
+    const float v = Elt<IT>::load1(a.dt, (long)(g0 + lane) * H + hh) + (a.dt_bias ? a.dt_bias[hh] : 0.f);
+    a.dt_ring[((long)sl * H + hh) * L + wl] = a.dt_softplus ? softplus_f32(v) : v;
+  }
+}
+
 template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY, bool SR, int PER>
 __global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
     mamba2_decode_kernel(const Mamba2Args a) {
@@ -347,6 +408,10 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
       if (a.next_is_flush) a.next_is_flush[b] = (nw == L - 1) ? 1 : 0;
     }
     if (st && a.status) atomicOr(a.status, st);
+  }
+  if (REPLAY && L > 1 && (rank & 63) == 0) {
+    const int nb = gridDim.x / H;
+    group_appends<IT, P, N, NT>(a, rank, nb - rank < 64 ? nb - rank : 64, h, L, tid);
   }
   const long yoff = ((long)b * H + h) * P;
   if (bad_slot) {
@@ -440,22 +505,6 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     finish_dt();
-    // append the current step at ring position w (replay only: the standard
-    // update has no ring and never reaches this branch)
-    if (REPLAY && wave == 0) {
-      const bool b_writer = (h % a.hpg) == 0;  // one writer per group
-      for (int k = lane; k < XV + BV; k += 64) {
-        if (k < XV) {
-          const u32x4 v = *reinterpret_cast<const u32x4*>(xs + ((long)w * XV + k) * 16);
-          st16(a.x_ring, ((xring0 + (long)w * P) * kIo) + k * 16, v);
-        } else if (b_writer) {
-          const int cb = k - XV;
-          const u32x4 v = *reinterpret_cast<const u32x4*>(Bs + ((long)w * BV + cb) * 16);
-          st16(a.B_ring, ((bring0 + (long)w * N) * kIo) + cb * 16, v);
-        }
-      }
-      if (lane == w) a.dt_ring[dtring0 + w] = dti;
-    }
     // decay weights: wt_i = dt_i * exp(A * sum_{i<j<=w} dt_j)
     const float rsuf = L <= 16 ? row16_suffix_exclusive(dti) : wave_suffix_exclusive(dti, lane);
     cumdecay = expf(Ah * lane_value(dti + rsuf, 0));
