@@ -27,6 +27,9 @@
 //  * the flush branch depends only on the row, so it is uniform across the
 //    workgroup: flush tiles fold the ring into their registers in
 //    double-buffered chunks and store the new state, the others only read;
+//  * ring appends (x, B, dt of the current step) are not written by each
+//    tile: the tiles of the first row of every 64-row group each append one
+//    head for all rows of the group before their own work (group_appends);
 //  * blockIdx is remapped so each XCD works on a contiguous range of rows.
 #pragma once
 

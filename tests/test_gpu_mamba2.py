@@ -288,3 +288,72 @@ def test_output_only_rows_never_write_the_pool():
     assert torch.equal(before[used], d["state"][used])
     assert torch.isnan(d["state"][unused]).all()
     assert wp.tolist() == [6] * 6 and fl.tolist() == [0] * 6
+
+
+@pytest.mark.parametrize("nb,H,P,N,G,L,io", [
+    (110, 6, 64, 32, 3, 5, "bf16"), (70, 80, 64, 16, 1, 16, "f32"), (4, 8, 64, 16, 2, 4, "f32")])
+def test_ring_appends_of_every_row(nb, H, P, N, G, L, io):
+    """Every row that does not flush gets ring entry w: its x and B rows bit
+    for bit (B once per group) and its dt after bias and softplus; every
+    other ring element keeps its bits.  All rows and all ring elements are
+    checked over several steps, with a full and a ragged 64-row group, more
+    heads than rows in a group, and rows forced to flush early."""
+    import linear_recurrence_amd as R
+    from oracle import numerics as ON
+    from workloads import TORCH_DTYPES
+    print(f"case: ring appends nb={nb} H={H} P={P} N={N} G={G} L={L} io={io}", flush=True)
+    dev = torch.device("cuda:0")
+    wl = Mamba2Workload(f"appends_b{nb}_h{H}", nb, H, P, N, G, L, 4, 2 * nb + 8, io, "f32",
+                        2500 + nb, desync=True)
+    gen = Mamba2Inputs(wl)
+    prm = {k: v.to(dev) for k, v in gen.params().items()}
+    slots = gen.slot_idx()
+    ns, iot = wl.num_slots, TORCH_DTYPES[io]
+    state = gen.state_pool(slots.tolist()).to(dev)
+    g = torch.Generator().manual_seed(2600 + nb)
+    # rings hold arbitrary earlier contents: any element not appended must keep its bits
+    xr = torch.randn((ns, H, L, P), generator=g).to(iot).to(dev)
+    dr = torch.rand((ns, H, L), generator=g).to(dev)
+    br = torch.randn((ns, G, L, N), generator=g).to(iot).to(dev)
+    wp = gen.start_positions().to(dev)
+    fl = (wp == L - 1).to(torch.uint8)
+    fl |= (torch.rand(nb, generator=g) < 0.2).to(torch.uint8).to(dev)  # forced flushes
+    nwp, nfl = torch.empty_like(wp), torch.empty_like(fl)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    s_np = slots.numpy()
+    bias = prm["dt_bias"].double().cpu().numpy()
+    for t in range(wl.steps):
+        inp = {k: v.to(dev) for k, v in gen.step(t).items()}
+        xr0, dr0, br0 = xr.clone(), dr.clone(), br.clone()
+        w_np, f_np = wp.cpu().numpy(), fl.cpu().numpy()
+        R.replayssm_decode(state, xr, dr, br, slots.to(dev), wp, fl, inp["x"], inp["dt"],
+                           prm["A"], inp["B"], inp["C"], D=prm["D"], z=inp["z"],
+                           dt_bias=prm["dt_bias"], next_write_pos=nwp, next_is_flush=nfl,
+                           status=status)
+        torch.cuda.synchronize()
+        exp_x, exp_b, exp_d = xr0.clone(), br0.clone(), dr0.clone()
+        dt_in = inp["dt"].double().cpu().numpy()
+        app_rows = [r for r in range(nb) if not f_np[r] and w_np[r] <= L - 2]
+        for r in app_rows:
+            s, w = int(s_np[r]), int(w_np[r])
+            exp_x[s, :, w, :] = inp["x"][r]
+            exp_b[s, :, w, :] = inp["B"][r]
+            exp_d[s, :, w] = torch.from_numpy(ON.softplus(dt_in[r] + bias)).float()
+        assert torch.equal(xr.view(torch.int8 if io == "f32" else torch.int16),
+                           exp_x.view(torch.int8 if io == "f32" else torch.int16)), f"step {t}: x ring"
+        assert torch.equal(br.view(torch.int8 if io == "f32" else torch.int16),
+                           exp_b.view(torch.int8 if io == "f32" else torch.int16)), f"step {t}: B ring"
+        mask = torch.zeros((ns, H, L), dtype=torch.bool)
+        for r in app_rows:
+            mask[int(s_np[r]), :, int(w_np[r])] = True
+        got_d, ref_d = dr.cpu(), exp_d.cpu()
+        assert torch.equal(got_d[~mask].view(torch.int32), ref_d[~mask].view(torch.int32)), \
+            f"step {t}: dt ring elements that were not appended changed"
+        if app_rows:
+            err = ((got_d[mask].double() - ref_d[mask].double()).abs()
+                   / ref_d[mask].double().abs().clamp(min=1.0)).max().item()
+            assert err <= 1e-6, f"step {t}: dt ring append error {err:.3e}"
+        log(f"step {t}: {len(app_rows)} of {nb} rows appended, rings exact")
+        wp, nwp = nwp, wp
+        fl, nfl = nfl, fl
+    assert int(status.item()) == 0
