@@ -297,7 +297,10 @@ def test_ring_appends_of_every_row(nb, H, P, N, G, L, io):
     for bit (B once per group) and its dt after bias and softplus; every
     other ring element keeps its bits.  All rows and all ring elements are
     checked over several steps, with a full and a ragged 64-row group, more
-    heads than rows in a group, and rows forced to flush early."""
+    heads than rows in a group, rows forced to flush early, and rows with bad
+    metadata (a full ring without the flush flag and a write position past
+    the ring at step 0, a slot out of range throughout), which must not
+    append."""
     import linear_recurrence_amd as R
     from oracle import numerics as ON
     from workloads import TORCH_DTYPES
@@ -318,6 +321,11 @@ def test_ring_appends_of_every_row(nb, H, P, N, G, L, io):
     wp = gen.start_positions().to(dev)
     fl = (wp == L - 1).to(torch.uint8)
     fl |= (torch.rand(nb, generator=g) < 0.2).to(torch.uint8).to(dev)  # forced flushes
+    # bad metadata: row 1 at the last position without the flag (overflow),
+    # row 2 past the ring, row 3 (when present) with a slot out of range
+    wp[1], fl[1], wp[2] = L - 1, 0, L + 3
+    if nb > 3:
+        slots[3] = -1
     nwp, nfl = torch.empty_like(wp), torch.empty_like(fl)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     s_np = slots.numpy()
@@ -333,7 +341,8 @@ def test_ring_appends_of_every_row(nb, H, P, N, G, L, io):
         torch.cuda.synchronize()
         exp_x, exp_b, exp_d = xr0.clone(), br0.clone(), dr0.clone()
         dt_in = inp["dt"].double().cpu().numpy()
-        app_rows = [r for r in range(nb) if not f_np[r] and w_np[r] <= L - 2]
+        app_rows = [r for r in range(nb)
+                    if not f_np[r] and 0 <= w_np[r] <= L - 2 and 0 <= s_np[r] < ns]
         for r in app_rows:
             s, w = int(s_np[r]), int(w_np[r])
             exp_x[s, :, w, :] = inp["x"][r]
@@ -356,4 +365,5 @@ def test_ring_appends_of_every_row(nb, H, P, N, G, L, io):
         log(f"step {t}: {len(app_rows)} of {nb} rows appended, rings exact")
         wp, nwp = nwp, wp
         fl, nfl = nfl, fl
-    assert int(status.item()) == 0
+    bits = R.ST_RING_OVERFLOW | R.ST_BAD_WRITE_POS | (R.ST_BAD_SLOT if nb > 3 else 0)
+    assert int(status.item()) == bits
