@@ -291,7 +291,8 @@ def test_output_only_rows_never_write_the_pool():
 
 
 @pytest.mark.parametrize("nb,H,P,N,G,L,io", [
-    (110, 6, 64, 32, 3, 5, "bf16"), (70, 80, 64, 16, 1, 16, "f32"), (4, 8, 64, 16, 2, 4, "f32")])
+    (110, 6, 64, 32, 3, 5, "bf16"), (70, 80, 64, 16, 1, 16, "f32"), (4, 8, 64, 16, 2, 4, "f32"),
+    (130, 64, 64, 128, 1, 16, "bf16")])  # the last: 16 vectors per lane, two waves per tile
 def test_ring_appends_of_every_row(nb, H, P, N, G, L, io):
     """Every row that does not flush gets ring entry w: its x and B rows bit
     for bit (B once per group) and its dt after bias and softplus; every
