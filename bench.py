@@ -1,6 +1,8 @@
 """Decode throughput of the ReplaySSM kernels on one MI355X.
 
-Headline: Mamba2 ReplaySSM decode (replayssm_decode) at batch 512, 80 heads,
+Headline: Mamba2 ReplaySSM decode (replayssm_decode_ordered: replayssm_decode
+with the host's flush-first row order, built per step phase by the library's
+host helper from the flush flags) at batch 512, 80 heads,
 headdim 64, dstate 128, ngroups 1, ring L = 16, bf16 inputs and bf16 state
 pool (fp32 arithmetic), start positions uniform in [0, L) so flush rows
 interleave every step.  One step = one replayssm_decode launch over the whole
@@ -10,7 +12,8 @@ other layers' ~2.7 GB have streamed (far beyond the 256 MB last-level cache).
 value = batch * steps / seconds (state-updates/s: one row advanced one step
 through one layer).
 
-Also measured in the same run (separate timed regions): the standard
+Also measured in the same run (separate timed regions): the plain
+replayssm_decode (no row order; same results, bit for bit); the standard
 read+write update (ssu_standard_decode) on the same workload; both again
 with stochastic rounding of the bf16 write-back; one tensor-parallel rank's
 share of the layer (10 of 80 heads); the GDN replay/standard decode at
@@ -109,9 +112,23 @@ class Mamba2Layers:
         for l in range(self.nl):
             assert np.array_equal(self.wp[l].cpu().numpy(), self.w0), "warm-up cursors"
 
-    def replay(self, l, inp, sr=None):
+    def phase_orders(self):
+        """Flush-first row orders for each step phase k (mod L) after the
+        warm-up: row r flushes at phase k iff (w0[r] + k) % L == L-1, the flag
+        the host metadata path holds; built by the library's host helper."""
+        import linear_recurrence_amd as R
+        L = self.wl.ring_len
+        out = []
+        for k in range(L):
+            fl = ((self.w0 + k) % L == L - 1).astype(np.uint8)
+            out.append(torch.from_numpy(R.flush_first_order(fl)).to(self.dev))
+        return out
+
+    def replay(self, l, inp, sr=None, order=None):
         import linear_recurrence_amd as R
         kw = {} if sr is None else dict(rounding="stochastic", sr_seed=17, sr_offset=sr)
+        if order is not None:
+            kw["row_order"] = order
         R.replayssm_decode(self.state[l], self.xr[l], self.dr[l], self.br[l], self.slots,
                            self.wp[l], self.fl[l], inp["x"], inp["dt"], self.prm["A"],
                            inp["B"], inp["C"], D=self.prm["D"], z=inp["z"],
@@ -127,13 +144,14 @@ class Mamba2Layers:
                               inp["B"], inp["C"], D=self.prm["D"], z=inp["z"],
                               dt_bias=self.prm["dt_bias"], y=self.y, **kw)
 
-    def replay_bytes(self, step_in_layer):
-        """Algorithmic bytes of one replay launch, from every row's cursor."""
+    def replay_bytes(self, step_in_layer, ordered=False):
+        """Algorithmic bytes of one replay launch, from every row's cursor
+        (plus the 4-byte row order entry when the launch takes one)."""
         L = self.wl.ring_len
         w = (self.w0 + step_in_layer) % L
         flush = w == L - 1
         per_row = (self.tile + w * self.entry + np.where(flush, self.tile, self.entry)
-                   + self.inp + 14)
+                   + self.inp + 14 + (4 if ordered else 0))
         return float(per_row.sum() + self.params)
 
     def standard_bytes(self):
@@ -156,31 +174,36 @@ def time_region(fn, steps, warmup):
     return e0.elapsed_time(e1) / 1e3  # seconds
 
 
-def bench_mamba2(wl, layers, steps, warmup, y_dtype, dev, sr=False):
+def bench_mamba2(wl, layers, steps, warmup, y_dtype, dev, sr=False, unordered=True):
     """Replay and standard timed regions; with sr, also both with stochastic
-    rounding of the bf16 write-back (a fresh Philox offset every call)."""
+    rounding of the bf16 write-back (a fresh Philox offset every call).  The
+    replay launches take the host's flush-first row order
+    (replayssm_decode_ordered); with unordered, the plain replayssm_decode is
+    timed too."""
     M = Mamba2Layers(wl, layers, dev, y_dtype)
     M.warm_rings()
+    orders = M.phase_orders()
     # replay: step i uses layer i % layers; bytes are accounted per launch
     # from the cursors that layer has at that step
     step_of = [0] * layers
 
-    def rep(i, sr_on=False):
+    def rep(i, sr_on=False, ordered=True):
         l = i % layers
-        M.replay(l, M.inputs[i % 8], sr=i if sr_on else None)
+        order = orders[step_of[l] % wl.ring_len] if ordered else None
+        M.replay(l, M.inputs[i % 8], sr=i if sr_on else None, order=order)
         step_of[l] += 1
 
-    def replay_region(first, sr_on):
+    def replay_region(first, sr_on, ordered=True):
         for i in range(warmup):
-            rep(first + i, sr_on)
+            rep(first + i, sr_on, ordered)
         torch.cuda.synchronize()
         local = list(step_of)
         total = 0.0
         for i in range(steps):
             l = (first + warmup + i) % layers
-            total += M.replay_bytes(local[l])
+            total += M.replay_bytes(local[l], ordered)
             local[l] += 1
-        t = time_region(lambda i: rep(first + warmup + i, sr_on), steps, 0)
+        t = time_region(lambda i: rep(first + warmup + i, sr_on, ordered), steps, 0)
         for l in range(layers):
             got = M.wp[l].cpu().numpy()
             assert np.array_equal(got, (M.w0 + step_of[l]) % wl.ring_len), "cursor drift"
@@ -202,6 +225,15 @@ def bench_mamba2(wl, layers, steps, warmup, y_dtype, dev, sr=False):
         "replay_GBps": rep_bytes * steps / t_rep / 1e9,
         "standard_GBps": std_bytes * steps / t_std / 1e9,
     }
+    if unordered:
+        t_pl, pl_bytes = replay_region(2 * (warmup + steps), False, ordered=False)
+        res["replay_unordered"] = {
+            "entry_point": "replayssm_decode",
+            "ms_per_step": t_pl / steps * 1e3,
+            "state_updates_per_s": nb * steps / t_pl,
+            "achieved_GBps": pl_bytes * steps / t_pl / 1e9,
+            "frac": pl_bytes * steps / t_pl / 1e9 / PEAK_HBM_GBPS,
+        }
     if sr:
         t_rsr, rsr_bytes = replay_region(warmup + steps, True)
         t_ssr = time_region(lambda i: std(i, True), steps, warmup)
@@ -465,7 +497,13 @@ def metadata_rate(rows, L, calls=2000):
         R.build_metadata(pos, base, L, align_block=16)
         pos += 1
     dt = time.perf_counter() - t0
+    fl = (rng.random(rows) < 1.0 / L).astype(np.uint8)
+    t0 = time.perf_counter()
+    for _ in range(calls):
+        R.flush_first_order(fl)
+    dto = time.perf_counter() - t0
     return {"rows_per_s": rows * calls / dt, "rows": rows, "calls": calls,
+            "flush_first_order_rows_per_s": rows * calls / dto,
             "note": "host C++ through the Python binding, one core"}
 
 
@@ -517,6 +555,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-sr", action="store_true",
                     help="skip the stochastic-rounding measurement")
+    ap.add_argument("--no-unordered", action="store_true",
+                    help="skip the plain replayssm_decode region (no host row order)")
     ap.add_argument("--no-tp", action="store_true",
                     help="skip the one-rank tensor-parallel share (10 heads)")
     args = ap.parse_args()
@@ -551,7 +591,8 @@ def main():
     y_dtype = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
     print(f"[bench] {wl.name}: layers={args.layers} steps={args.steps} warmup={args.warmup}",
           file=sys.stderr, flush=True)
-    m = bench_mamba2(wl, args.layers, args.steps, args.warmup, y_dtype, dev, sr=not args.no_sr)
+    m = bench_mamba2(wl, args.layers, args.steps, args.warmup, y_dtype, dev, sr=not args.no_sr,
+                     unordered=not args.no_unordered)
     print(f"[bench] mamba2 done: {m['replay_GBps']:.0f} GB/s replay, "
           f"{m['standard_GBps']:.0f} GB/s standard", file=sys.stderr, flush=True)
     tp = None
@@ -560,7 +601,7 @@ def main():
         # 16 rotated layers so the working set stays far above the last-level cache
         wl_tp = dataclasses.replace(wl, name="mamba2_b512_h10_L16_bf16state_tp8share",
                                     nheads=10)
-        t = bench_mamba2(wl_tp, 16, args.steps, args.warmup, y_dtype, dev)
+        t = bench_mamba2(wl_tp, 16, args.steps, args.warmup, y_dtype, dev, unordered=False)
         tp = {"workload": wl_tp.name, "nheads": 10, "layers_rotated": 16,
               "replay_updates_per_s": t["replay_updates_per_s"],
               "replay_GBps": t["replay_GBps"], "replay_frac": t["replay_GBps"] / PEAK_HBM_GBPS,
@@ -614,7 +655,7 @@ def main():
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
             "traffic_source": traffic_note,
-            "kernel": "replayssm_decode (mamba2_decode_kernel, replay)",
+            "kernel": "replayssm_decode_ordered (mamba2_decode_kernel, replay)",
             "algorithmic_bytes_per_launch": m["replay_bytes_per_launch"],
         },
         "cpu_baseline": cpu,
@@ -628,6 +669,7 @@ def main():
             "bytes_per_launch": m["standard_bytes_per_launch"],
         },
         "speedup_vs_standard": m["replay_updates_per_s"] / m["standard_updates_per_s"],
+        "replay_unordered": m.get("replay_unordered"),
         "gdn": gdn,
         "kda": kda,
         "gdn_spec": spec,

@@ -76,7 +76,7 @@ enum {
   RSSM_ST_BAD_WRITE_POS = 1, /* write_pos outside [0, L): clamped, row flushed */
   RSSM_ST_RING_OVERFLOW = 2, /* write_pos == L-1 without is_flush: row flushed */
   RSSM_ST_BAD_SLOT = 4,      /* slot index outside [0, num_slots): row skipped */
-  RSSM_ST_BAD_ROW = 8        /* ring reset: row index outside [0, batch) */
+  RSSM_ST_BAD_ROW = 8        /* ring reset or row order: row index outside [0, batch) */
 };
 
 /*
@@ -180,6 +180,30 @@ int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring,
                      const void* B, const void* C, const float* D,
                      const void* z, const float* dt_bias, void* y,
                      int32_t* status, hipStream_t stream);
+
+/*
+ * replayssm_decode_ordered - replayssm_decode with the batch rows handed in
+ * flush-first order by the host (not on the pages: a scheduling hint for
+ * this GPU).  row_order [batch] int32 (device pointer) must be a
+ * permutation of 0..batch-1; replayssm_flush_first_order builds it from the
+ * flush flags the host metadata path already has.  The results are those
+ * of replayssm_decode for any permutation; the order only decides which
+ * rows each of the GPU's eight dies (XCDs) takes: the positions of the list
+ * are dealt to them in turn, so each takes an equal share of the flush rows,
+ * first (replayssm_decode spreads them by aligned groups of 64 rows, whose
+ * shares vary from step to step).  An entry outside [0, batch) is clamped
+ * and sets RSSM_ST_BAD_ROW; a list that repeats a row leaves another row
+ * unprocessed (its y and next cursors unspecified).  row_order == NULL:
+ * RSSM_EINVAL.
+ */
+int replayssm_decode_ordered(const rssm_dims* dims, void* state, void* x_ring,
+                             float* dt_ring, void* B_ring, const int32_t* slot_idx,
+                             const int32_t* write_pos, const uint8_t* is_flush,
+                             int32_t* next_write_pos, uint8_t* next_is_flush,
+                             const void* x, const void* dt, const float* A, const void* B,
+                             const void* C, const float* D, const void* z,
+                             const float* dt_bias, void* y, const int32_t* row_order,
+                             int32_t* status, hipStream_t stream);
 
 /*
  * replayssm_ring_reset - rows whose slot just received a fresh checkpoint
@@ -367,6 +391,14 @@ int replayssm_build_metadata(int32_t n_rows, int32_t ring_len, int32_t align_blo
  * slot, reset that row's cursors with replayssm_ring_reset.
  */
 int replayssm_check_copy_sources(int32_t n, const int32_t* src_write_pos);
+
+/*
+ * replayssm_flush_first_order - the row order for replayssm_decode_ordered:
+ * the rows with is_flush[r] != 0 in increasing r, then the others in
+ * increasing r.  is_flush [n_rows] and row_order [n_rows] are HOST pointers.
+ * RSSM_OK, or RSSM_EINVAL for n_rows < 0 or a NULL pointer with n_rows > 0.
+ */
+int replayssm_flush_first_order(int32_t n_rows, const uint8_t* is_flush, int32_t* row_order);
 
 /* Human-readable text of a return code (static storage). */
 const char* replayssm_strerror(int code);

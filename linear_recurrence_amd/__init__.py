@@ -21,7 +21,7 @@ __all__ = [
     "ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
     "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
     "replayssm_gdn_spec_commit", "kda_standard_decode", "replayssm_kda_decode",
-    "build_metadata",
+    "build_metadata", "flush_first_order",
     "check_copy_sources", "library_path", "load",
     "RssmError", "ST_BAD_WRITE_POS", "ST_RING_OVERFLOW", "ST_BAD_SLOT",
     "ST_BAD_ROW", "EXPORTS",
@@ -34,7 +34,7 @@ ST_BAD_WRITE_POS, ST_RING_OVERFLOW, ST_BAD_SLOT, ST_BAD_ROW = 1, 2, 4, 8
 EXPORTS = ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
            "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
            "replayssm_gdn_spec_commit", "kda_standard_decode", "replayssm_kda_decode",
-           "replayssm_build_metadata",
+           "replayssm_build_metadata", "replayssm_decode_ordered", "replayssm_flush_first_order",
            "replayssm_check_copy_sources", "replayssm_strerror", "replayssm_abi_version")
 
 _DT = {torch.float32: F32, torch.bfloat16: BF16}
@@ -83,6 +83,10 @@ def load():
     I = ctypes.c_int32
     lib.ssu_standard_decode.argtypes = [ctypes.POINTER(Dims)] + [P] * 13
     lib.replayssm_decode.argtypes = [ctypes.POINTER(Dims)] + [P] * 20
+    lib.replayssm_decode_ordered.argtypes = [ctypes.POINTER(Dims)] + [P] * 21
+    lib.replayssm_decode_ordered.restype = ctypes.c_int
+    lib.replayssm_flush_first_order.argtypes = [I, P, P]
+    lib.replayssm_flush_first_order.restype = ctypes.c_int
     lib.replayssm_ring_reset.argtypes = [ctypes.POINTER(Dims), P, P, P, I, P, P]
     lib.gdn_standard_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 10
     lib.replayssm_gdn_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 17
@@ -197,13 +201,16 @@ def replayssm_decode(state, x_ring, dt_ring, B_ring, slot_idx, write_pos,
                      is_flush, x, dt, A, B, C, D=None, z=None, dt_bias=None,
                      y=None, next_write_pos=None, next_is_flush=None,
                      dt_softplus=True, status=None, out_dtype=None, rounding="nearest",
-                     sr_seed=0, sr_offset=0, stream=None):
+                     sr_seed=0, sr_offset=0, stream=None, row_order=None):
     """One ReplaySSM output-only decode step; returns y.
 
     Rings: x_ring [slots, H, L, P] (io dtype), dt_ring [slots, H, L] float32,
     B_ring [slots, G, L, N] (io dtype).  Cursors: write_pos int32 [batch],
     is_flush uint8 [batch]; the next cursors are written to next_write_pos /
-    next_is_flush when given.
+    next_is_flush when given.  row_order (int32 [batch] on the device, a
+    permutation of the rows, flush rows first: see flush_first_order) selects
+    replayssm_decode_ordered, which gives the same results with the flush
+    rows spread evenly over the GPU's dies.
     """
     dev = _need(state, "state").device
     ns, H, P, N = state.shape
@@ -235,12 +242,18 @@ def replayssm_decode(state, x_ring, dt_ring, B_ring, slot_idx, write_pos,
         y = torch.empty((nb, H, P), dtype=out_dtype or io, device=dev)
     _need(y, "y", (torch.float32, torch.bfloat16), (nb, H, P), dev=dev)
     d = _mamba2_dims(state, x, B, L, y.dtype, dt_softplus, rounding, sr_seed, sr_offset)
-    rc = load().replayssm_decode(
-        ctypes.byref(d), _ptr(state), _ptr(x_ring), _ptr(dt_ring), _ptr(B_ring),
-        _ptr(slot_idx), _ptr(write_pos), _ptr(is_flush), _ptr(next_write_pos),
-        _ptr(next_is_flush), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
-        _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(y), _ptr(status), _stream(stream))
-    _check("replayssm_decode", rc)
+    args = [ctypes.byref(d), _ptr(state), _ptr(x_ring), _ptr(dt_ring), _ptr(B_ring),
+            _ptr(slot_idx), _ptr(write_pos), _ptr(is_flush), _ptr(next_write_pos),
+            _ptr(next_is_flush), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+            _ptr(D), _ptr(z), _ptr(dt_bias), _ptr(y)]
+    if row_order is None:
+        rc = load().replayssm_decode(*args, _ptr(status), _stream(stream))
+        _check("replayssm_decode", rc)
+    else:
+        _need(row_order, "row_order", torch.int32, (nb,), dev=dev)
+        rc = load().replayssm_decode_ordered(*args, _ptr(row_order), _ptr(status),
+                                             _stream(stream))
+        _check("replayssm_decode_ordered", rc)
     return y
 
 
@@ -289,6 +302,20 @@ def build_metadata(pos, decode_base, ring_len, force_flush=None, align_block=0):
         ctypes.c_void_p(fl.ctypes.data) if n else None)
     _check("replayssm_build_metadata", rc)
     return wp, fl
+
+
+def flush_first_order(is_flush):
+    """Row order for replayssm_decode(row_order=...): the flush rows, then the
+    others, each in increasing row index.  is_flush: uint8 numpy [n] (host);
+    returns an int32 numpy [n]."""
+    import numpy as np
+    n = is_flush.shape[0] if hasattr(is_flush, "shape") else 0
+    fp = _host(is_flush, "is_flush", np.uint8)
+    order = np.zeros(n, np.int32)
+    rc = load().replayssm_flush_first_order(
+        ctypes.c_int32(n), fp, ctypes.c_void_p(order.ctypes.data) if n else None)
+    _check("replayssm_flush_first_order", rc)
+    return order
 
 
 def check_copy_sources(src_write_pos):

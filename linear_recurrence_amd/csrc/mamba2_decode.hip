@@ -92,13 +92,12 @@ extern "C" int ssu_standard_decode(const rssm_dims* dims, void* state, const int
   return dispatch(false, a, *dims, stream);
 }
 
-extern "C" int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring, float* dt_ring,
-                                void* B_ring, const int32_t* slot_idx, const int32_t* write_pos,
-                                const uint8_t* is_flush, int32_t* next_write_pos,
-                                uint8_t* next_is_flush, const void* x, const void* dt,
-                                const float* A, const void* B, const void* C, const float* D,
-                                const void* z, const float* dt_bias, void* y, int32_t* status,
-                                hipStream_t stream) {
+static int replay_entry(const rssm_dims* dims, void* state, void* x_ring, float* dt_ring,
+                        void* B_ring, const int32_t* slot_idx, const int32_t* write_pos,
+                        const uint8_t* is_flush, int32_t* next_write_pos, uint8_t* next_is_flush,
+                        const void* x, const void* dt, const float* A, const void* B,
+                        const void* C, const float* D, const void* z, const float* dt_bias,
+                        void* y, const int32_t* row_order, int32_t* status, hipStream_t stream) {
   int rc = check_dims(dims, true);
   if (rc) return rc;
   if (dims->batch == 0) return RSSM_OK;  // empty batch: nothing to read or write
@@ -138,7 +137,35 @@ extern "C" int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring
   a.dt_softplus = dims->dt_softplus;
   a.sr_seed = dims->sr_seed;
   a.sr_offset = dims->sr_offset;
+  a.row_order = row_order;
   return dispatch(true, a, *dims, stream);
+}
+
+extern "C" int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring, float* dt_ring,
+                                void* B_ring, const int32_t* slot_idx, const int32_t* write_pos,
+                                const uint8_t* is_flush, int32_t* next_write_pos,
+                                uint8_t* next_is_flush, const void* x, const void* dt,
+                                const float* A, const void* B, const void* C, const float* D,
+                                const void* z, const float* dt_bias, void* y, int32_t* status,
+                                hipStream_t stream) {
+  return replay_entry(dims, state, x_ring, dt_ring, B_ring, slot_idx, write_pos, is_flush,
+                      next_write_pos, next_is_flush, x, dt, A, B, C, D, z, dt_bias, y, nullptr,
+                      status, stream);
+}
+
+extern "C" int replayssm_decode_ordered(const rssm_dims* dims, void* state, void* x_ring,
+                                        float* dt_ring, void* B_ring, const int32_t* slot_idx,
+                                        const int32_t* write_pos, const uint8_t* is_flush,
+                                        int32_t* next_write_pos, uint8_t* next_is_flush,
+                                        const void* x, const void* dt, const float* A,
+                                        const void* B, const void* C, const float* D,
+                                        const void* z, const float* dt_bias, void* y,
+                                        const int32_t* row_order, int32_t* status,
+                                        hipStream_t stream) {
+  if (!row_order) return RSSM_EINVAL;
+  return replay_entry(dims, state, x_ring, dt_ring, B_ring, slot_idx, write_pos, is_flush,
+                      next_write_pos, next_is_flush, x, dt, A, B, C, D, z, dt_bias, y, row_order,
+                      status, stream);
 }
 
 namespace rssm {
@@ -190,4 +217,4 @@ extern "C" const char* replayssm_strerror(int code) {
   return "unknown error";
 }
 
-extern "C" int replayssm_abi_version(void) { return 101; }
+extern "C" int replayssm_abi_version(void) { return 102; }

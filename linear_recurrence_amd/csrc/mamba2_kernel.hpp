@@ -38,6 +38,37 @@
 
 namespace rssm {
 
+// Row metadata of a replay tile when the host supplies the rows in
+// flush-first order (row_order: a permutation of 0..nb-1 listing the flush
+// rows first).  The positions of that list are dealt to the eight XCD rank
+// ranges in turn, so each XCD receives an equal share of the flush rows and
+// takes them first; with each aligned 64-row group taking only its own
+// flush rows, the XCDs' shares vary from step to step and the launch waits
+// for the one with the most.  The map rank -> position is a bijection for
+// any batch, so any permutation gives the same results; an entry outside
+// [0, nb) is clamped and reported as RSSM_ST_BAD_ROW.  The row order and
+// the row's metadata arrive by scalar loads.
+typedef __attribute__((address_space(4))) const int32_t kconst_i32;
+__device__ static inline RowPick dealt_order_pick(int rank, int nb, const int32_t* row_order,
+                                                  const int32_t* slot_idx,
+                                                  const int32_t* write_pos,
+                                                  const uint8_t* is_flush, int& st) {
+  // ranks fill the residue classes of the positions mod 8 in turn: class x
+  // holds ranks [x*q + min(x, m), +q + (x < m)) and positions x, x+8, ...
+  const int q = nb >> 3, m = nb & 7;
+  int x = 0;
+#pragma unroll
+  for (int c = 1; c < 8; ++c)
+    if (rank >= c * q + (c < m ? c : m)) x = c;
+  const int pos = (rank - (x * q + (x < m ? x : m))) * 8 + x;
+  int b = *(kconst_i32*)(row_order + pos);
+  if (b < 0 || b >= nb) {
+    st |= RSSM_ST_BAD_ROW;
+    b = b < 0 ? 0 : nb - 1;
+  }
+  return {b, *(kconst_i32*)(slot_idx + b), *(kconst_i32*)(write_pos + b), is_flush[b] != 0};
+}
+
 struct Mamba2Args {
   void* state;
   void* x_ring;
@@ -66,6 +97,7 @@ struct Mamba2Args {
   int32_t dt_softplus;
   uint64_t sr_seed;    // stochastic rounding: Philox key (seed, offset)
   uint64_t sr_offset;
+  const int32_t* row_order;  // flush-first row order from the host, or NULL
 };
 
 // Tile geometry: PER target state vectors per lane.  The replay kernel
@@ -379,16 +411,21 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
   const int g = h / a.hpg;
 
   // ---- row metadata (uniform across the workgroup)
+  int st = 0;
   RowPick pick{rank, 0, 0, true};
-  if constexpr (REPLAY)
-    pick = flush_first_pick(rank, gridDim.x / H, a.slot_idx, a.write_pos, a.is_flush, lane);
-  else
+  if constexpr (REPLAY) {
+    if (a.row_order)
+      pick = dealt_order_pick(rank, gridDim.x / H, a.row_order, a.slot_idx, a.write_pos,
+                              a.is_flush, st);
+    else
+      pick = flush_first_pick(rank, gridDim.x / H, a.slot_idx, a.write_pos, a.is_flush, lane);
+  } else {
     pick.s = a.slot_idx[rank];
+  }
   const int b = pick.b;
   const int s = pick.s;
   int w = 0;
   bool f = true;
-  int st = 0;
   if (REPLAY) {
     w = pick.w;
     f = pick.f;

@@ -45,3 +45,16 @@ extern "C" int replayssm_check_copy_sources(int32_t n, const int32_t* src_write_
     if (src_write_pos[i] != 0) return RSSM_EINVAL;  // ring not empty: its entries would be lost
   return RSSM_OK;
 }
+
+extern "C" int replayssm_flush_first_order(int32_t n_rows, const uint8_t* is_flush,
+                                           int32_t* row_order) {
+  if (n_rows < 0) return RSSM_EINVAL;
+  if (n_rows == 0) return RSSM_OK;
+  if (!is_flush || !row_order) return RSSM_EINVAL;
+  int32_t k = 0;
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (is_flush[r]) row_order[k++] = r;  // flush rows first, in row order
+  for (int32_t r = 0; r < n_rows; ++r)
+    if (!is_flush[r]) row_order[k++] = r;  // then the others, in row order
+  return RSSM_OK;
+}

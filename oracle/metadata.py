@@ -45,3 +45,13 @@ def build_metadata(pos, decode_base, L, force_flush=None, align_block=0):
 def copy_sources_flushed(src_write_pos):
     """A slot may be copied only when its ring is empty (write position 0)."""
     return all(int(w) == 0 for w in src_write_pos)
+
+
+def flush_first_order(is_flush):
+    """The rows whose flush flag is nonzero in increasing index, then the
+    others in increasing index (a scheduling order for the decode launch,
+    not part of the method: the decode gives the same results for any
+    permutation of the rows)."""
+    n = len(is_flush)
+    return ([r for r in range(n) if int(is_flush[r]) != 0]
+            + [r for r in range(n) if int(is_flush[r]) == 0])

@@ -368,3 +368,76 @@ def test_ring_appends_of_every_row(nb, H, P, N, G, L, io):
         fl, nfl = nfl, fl
     bits = R.ST_RING_OVERFLOW | R.ST_BAD_WRITE_POS | (R.ST_BAD_SLOT if nb > 3 else 0)
     assert int(status.item()) == bits
+
+
+@pytest.mark.parametrize("nb,H,P,N,G,L", [(200, 8, 64, 32, 2, 8), (130, 64, 64, 128, 1, 16)])
+def test_row_order_gives_the_same_results(nb, H, P, N, G, L):
+    """replayssm_decode_ordered with the host's flush-first order, and with an
+    arbitrary permutation, gives bit for bit what replayssm_decode gives (y,
+    checkpoints, rings, cursors) over steps that cross flushes; a row index
+    outside the batch is clamped and reported.  Small grids (4 vectors per
+    lane) and full grids (16) with ragged 64-row groups."""
+    import linear_recurrence_amd as R
+    from workloads import TORCH_DTYPES
+    print(f"case: row order nb={nb} H={H} P={P} N={N} L={L}", flush=True)
+    dev = torch.device("cuda:0")
+    wl = Mamba2Workload(f"order_b{nb}_h{H}", nb, H, P, N, G, L, 2 * L + 3, 2 * nb + 8, "bf16",
+                        "bf16", 2700 + nb, desync=True)
+    gen = Mamba2Inputs(wl)
+    prm = {k: v.to(dev) for k, v in gen.params().items()}
+    slots = gen.slot_idx().to(dev)
+    iot = TORCH_DTYPES["bf16"]
+    pool = gen.state_pool(gen.slot_idx().tolist())
+    g = torch.Generator().manual_seed(2800 + nb)
+    perm = torch.randperm(nb, generator=g).to(torch.int32).to(dev)
+
+    def fresh():
+        ns = wl.num_slots
+        return {"state": pool.clone().to(dev),
+                "xr": torch.zeros((ns, H, L, P), dtype=iot, device=dev),
+                "dr": torch.zeros((ns, H, L), device=dev),
+                "br": torch.zeros((ns, G, L, N), dtype=iot, device=dev),
+                "wp": gen.start_positions().to(dev),
+                "fl": (gen.start_positions() == L - 1).to(torch.uint8).to(dev)}
+
+    runs = {"plain": fresh(), "flush_first": fresh(), "permuted": fresh()}
+    for t in range(wl.steps):
+        inp = {k: v.to(dev) for k, v in gen.step(t).items()}
+        ys = {}
+        for name, r in runs.items():
+            order = None
+            if name == "flush_first":
+                order = torch.from_numpy(R.flush_first_order(r["fl"].cpu().numpy())).to(dev)
+            elif name == "permuted":
+                order = perm
+            nwp, nfl = torch.empty_like(r["wp"]), torch.empty_like(r["fl"])
+            ys[name] = R.replayssm_decode(
+                r["state"], r["xr"], r["dr"], r["br"], slots, r["wp"], r["fl"], inp["x"],
+                inp["dt"], prm["A"], inp["B"], inp["C"], D=prm["D"], z=inp["z"],
+                dt_bias=prm["dt_bias"], next_write_pos=nwp, next_is_flush=nfl,
+                row_order=order)
+            r["wp"], r["fl"] = nwp, nfl
+        torch.cuda.synchronize()
+        ref = runs["plain"]
+        for name in ("flush_first", "permuted"):
+            r = runs[name]
+            assert torch.equal(ys[name].view(torch.int16), ys["plain"].view(torch.int16)), \
+                f"step {t} {name}: y"
+            for k in ("state", "xr", "br"):
+                assert torch.equal(r[k].view(torch.int16), ref[k].view(torch.int16)), \
+                    f"step {t} {name}: {k}"
+            assert torch.equal(r["dr"].view(torch.int32), ref["dr"].view(torch.int32))
+            assert torch.equal(r["wp"], ref["wp"]) and torch.equal(r["fl"], ref["fl"])
+    log(f"{wl.steps} steps: ordered launches equal the plain ones bit for bit")
+    # an entry outside the batch is clamped and reported
+    r = fresh()
+    bad = perm.clone()
+    bad[3] = nb + 5
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    inp = {k: v.to(dev) for k, v in gen.step(0).items()}
+    R.replayssm_decode(r["state"], r["xr"], r["dr"], r["br"], slots, r["wp"], r["fl"], inp["x"],
+                       inp["dt"], prm["A"], inp["B"], inp["C"], D=prm["D"], z=inp["z"],
+                       dt_bias=prm["dt_bias"], next_write_pos=torch.empty_like(r["wp"]),
+                       next_is_flush=torch.empty_like(r["fl"]), status=status, row_order=bad)
+    torch.cuda.synchronize()
+    assert int(status.item()) & R.ST_BAD_ROW

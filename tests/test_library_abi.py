@@ -37,7 +37,7 @@ def test_library_loads_and_exports_every_declared_symbol():
     for fn in sorted(_declared()):
         assert hasattr(lib, fn), f"{fn} is declared but not exported"
     assert set(R.EXPORTS) <= _declared()
-    assert lib.replayssm_abi_version() == 101
+    assert lib.replayssm_abi_version() == 102
     assert lib.replayssm_strerror(-4).decode().startswith("shape")
 
 

@@ -190,3 +190,26 @@ def test_copy_source_rule():
     R.check_copy_sources(np.zeros(0, np.int32))
     with pytest.raises(R.RssmError):
         R.check_copy_sources(np.array([0, 0, 3], np.int32))
+
+
+def test_oracle_flush_first_order_is_a_stable_partition():
+    """Flush rows first, each class in increasing row index: the same as a
+    stable sort on the key (flag == 0), and a permutation of the rows."""
+    rng = np.random.default_rng(5)
+    for n in (0, 1, 7, 64, 130):
+        fl = rng.integers(0, 3, n).astype(np.uint8)  # any nonzero value flushes
+        order = OMD.flush_first_order(fl)
+        assert sorted(order) == list(range(n))
+        assert order == np.argsort(fl == 0, kind="stable").tolist()
+        nf = int((fl != 0).sum())
+        assert all(fl[r] != 0 for r in order[:nf]) and all(fl[r] == 0 for r in order[nf:])
+
+
+def test_flush_first_order_helper_matches_oracle():
+    rng = np.random.default_rng(6)
+    for n in (0, 1, 5, 64, 100, 512):
+        for p in (0.0, 1.0 / 16, 0.5, 1.0):
+            fl = (rng.random(n) < p).astype(np.uint8) * rng.integers(1, 4, n).astype(np.uint8)
+            assert R.flush_first_order(fl).tolist() == OMD.flush_first_order(fl)
+    with pytest.raises(TypeError):
+        R.flush_first_order(np.zeros(4, np.int32))
