@@ -429,6 +429,22 @@ def test_row_order_gives_the_same_results(nb, H, P, N, G, L):
             assert torch.equal(r["dr"].view(torch.int32), ref["dr"].view(torch.int32))
             assert torch.equal(r["wp"], ref["wp"]) and torch.equal(r["fl"], ref["fl"])
     log(f"{wl.steps} steps: ordered launches equal the plain ones bit for bit")
+    # stochastic rounding of the write-back draws its bits by (slot, head,
+    # element), not by the order the rows are processed in
+    for t in range(wl.steps, wl.steps + L):
+        inp = {k: v.to(dev) for k, v in gen.step(t).items()}
+        for name in ("plain", "permuted"):
+            r = runs[name]
+            nwp, nfl = torch.empty_like(r["wp"]), torch.empty_like(r["fl"])
+            R.replayssm_decode(r["state"], r["xr"], r["dr"], r["br"], slots, r["wp"], r["fl"],
+                               inp["x"], inp["dt"], prm["A"], inp["B"], inp["C"], D=prm["D"],
+                               z=inp["z"], dt_bias=prm["dt_bias"], next_write_pos=nwp,
+                               next_is_flush=nfl, rounding="stochastic", sr_seed=31,
+                               sr_offset=t, row_order=perm if name == "permuted" else None)
+            r["wp"], r["fl"] = nwp, nfl
+    torch.cuda.synchronize()
+    assert torch.equal(runs["permuted"]["state"].view(torch.int16),
+                       runs["plain"]["state"].view(torch.int16)), "stochastic rounding: state"
     # an entry outside the batch is clamped and reported
     r = fresh()
     bad = perm.clone()
