@@ -1,8 +1,6 @@
 """Decode throughput of the ReplaySSM kernels on one MI355X.
 
-Headline: Mamba2 ReplaySSM decode (replayssm_decode_ordered: replayssm_decode
-with the host's flush-first row order, built per step phase by the library's
-host helper from the flush flags) at batch 512, 80 heads,
+Headline: Mamba2 ReplaySSM decode (replayssm_decode) at batch 512, 80 heads,
 headdim 64, dstate 128, ngroups 1, ring L = 16, bf16 inputs and bf16 state
 pool (fp32 arithmetic), start positions uniform in [0, L) so flush rows
 interleave every step.  One step = one replayssm_decode launch over the whole
@@ -10,19 +8,23 @@ batch for one layer; ``--layers`` independent layers (state pool + rings +
 cursors each) are used round-robin so a checkpoint is re-read only after the
 other layers' ~2.7 GB have streamed (far beyond the 256 MB last-level cache).
 value = batch * steps / seconds (state-updates/s: one row advanced one step
-through one layer).
+through one layer), from the median of ``--reps`` timed regions of exactly
+``--steps`` launches each.
 
-Also measured in the same run (separate timed regions): the plain
-replayssm_decode (no row order; same results, bit for bit); the standard
-read+write update (ssu_standard_decode) on the same workload; both again
-with stochastic rounding of the bf16 write-back; one tensor-parallel rank's
-share of the layer (10 of 80 heads); the GDN replay/standard decode at
-batch 256 (16 key / 32 value heads, K = V = 128, L = 16, bf16 q/k/v, fp32
-state) and its speculative verify + commit with 4 drafts per round; the KDA
+Also measured in the same run (separate timed regions, each repeated):
+replayssm_decode_ordered (the same step with the host's flush-first row
+order; same results, bit for bit); the standard read+write update
+(ssu_standard_decode) on the same workload; both again with stochastic
+rounding of the bf16 write-back; one tensor-parallel rank's share of the
+layer (10 of 80 heads); the GDN replay/standard decode at batch 256 (16 key
+/ 32 value heads, K = V = 128, L = 16, bf16 q/k/v, fp32 state) and its
+speculative verify + commit with 4 drafts per round; the KDA
 (per-key-channel gate) replay/standard decode at batch 256, 32 heads,
 K = V = 128, L = 16; the host metadata builder; and the float64 CPU oracle
-on a bounded sample, on one thread (``cpu_baseline``) and sharded by rows
-over up to 16 processes (``cpu_baseline_parallel``).
+on a bounded sample, both the ReplaySSM reconstruction and the standard
+recurrence on one thread (``cpu_baseline``, ``cpu_baseline_standard``) and
+the reconstruction sharded by rows over up to 16 processes
+(``cpu_baseline_parallel``), with the host's core count.
 
 Roofline: algorithmic bytes per launch (checkpoint reads, ring reads of the
 live entries, ring appends, flush write-backs, step inputs, outputs and
@@ -32,7 +34,7 @@ the average launch time measured with HIP events on the launch stream.
 WRITE_SIZE counters (profiles/replayssm_decode_mamba2_b512_traffic.json),
 reported only while its source fingerprint matches the kernel sources.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--layers 4]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--layers 4]
        python bench.py --copy-probe      (copy kernel for counter calibration)
 """
 
@@ -159,7 +161,9 @@ class Mamba2Layers:
 
 
 def time_region(fn, steps, warmup):
-    """W untimed steps, then exactly K timed steps between synchronisations."""
+    """W untimed steps, then exactly K timed steps between synchronisations.
+    The events are recorded on torch's current stream, which is the stream
+    the binding launches every kernel on."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -174,81 +178,103 @@ def time_region(fn, steps, warmup):
     return e0.elapsed_time(e1) / 1e3  # seconds
 
 
-def bench_mamba2(wl, layers, steps, warmup, y_dtype, dev, sr=False, unordered=True):
-    """Replay and standard timed regions; with sr, also both with stochastic
-    rounding of the bf16 write-back (a fresh Philox offset every call).  The
-    replay launches take the host's flush-first row order
-    (replayssm_decode_ordered); with unordered, the plain replayssm_decode is
-    timed too."""
+def timed_reps(fn, steps, warmup, reps):
+    """W untimed steps, then `reps` timed regions of exactly K steps each
+    (the step index keeps counting across regions); seconds per region."""
+    out = []
+    for r in range(reps):
+        out.append(time_region(lambda i: fn(r * steps + i + (0 if r == 0 else warmup)),
+                               steps, warmup if r == 0 else 0))
+    return out
+
+
+def median(v):
+    return float(np.median(np.asarray(v, dtype=np.float64)))
+
+
+def spread(v):
+    """Relative spread (max - min) / median of repeated measurements."""
+    v = np.asarray(v, dtype=np.float64)
+    return float((v.max() - v.min()) / np.median(v))
+
+
+def bench_mamba2(wl, layers, steps, warmup, y_dtype, dev, reps, sr=False, ordered=True):
+    """Timed regions of the replay (plain replayssm_decode: the headline),
+    the standard update and, with `ordered`, replayssm_decode_ordered with
+    the host's flush-first row lists; with sr, replay and standard again with
+    stochastic rounding of the bf16 write-back (a fresh Philox offset every
+    call).  Each kernel is timed in `reps` regions of `steps` launches; the
+    median region is reported with the spread."""
     M = Mamba2Layers(wl, layers, dev, y_dtype)
     M.warm_rings()
-    orders = M.phase_orders()
+    orders = M.phase_orders() if ordered else None
     # replay: step i uses layer i % layers; bytes are accounted per launch
     # from the cursors that layer has at that step
     step_of = [0] * layers
+    base = [0]
 
-    def rep(i, sr_on=False, ordered=True):
+    def rep(i, sr_on=False, use_order=False):
         l = i % layers
-        order = orders[step_of[l] % wl.ring_len] if ordered else None
+        order = orders[step_of[l] % wl.ring_len] if use_order else None
         M.replay(l, M.inputs[i % 8], sr=i if sr_on else None, order=order)
         step_of[l] += 1
 
-    def replay_region(first, sr_on, ordered=True):
+    def replay_regions(sr_on, use_order):
+        first = base[0]
         for i in range(warmup):
-            rep(first + i, sr_on, ordered)
+            rep(first + i, sr_on, use_order)
         torch.cuda.synchronize()
-        local = list(step_of)
-        total = 0.0
-        for i in range(steps):
-            l = (first + warmup + i) % layers
-            total += M.replay_bytes(local[l], ordered)
-            local[l] += 1
-        t = time_region(lambda i: rep(first + warmup + i, sr_on, ordered), steps, 0)
+        ts, bs = [], []
+        for r in range(reps):
+            local = list(step_of)
+            total = 0.0
+            start = first + warmup + r * steps
+            for i in range(steps):
+                l = (start + i) % layers
+                total += M.replay_bytes(local[l], use_order)
+                local[l] += 1
+            ts.append(time_region(lambda i: rep(start + i, sr_on, use_order), steps, 0))
+            bs.append(total / steps)
+        base[0] = first + warmup + reps * steps
         for l in range(layers):
             got = M.wp[l].cpu().numpy()
             assert np.array_equal(got, (M.w0 + step_of[l]) % wl.ring_len), "cursor drift"
-        return t, total / steps
+        return ts, bs
 
-    t_rep, rep_bytes = replay_region(0, False)
+    def summary(ts, bs, entry):
+        k = int(np.argsort(ts)[len(ts) // 2])  # the median region
+        gbps = [b * steps / t / 1e9 for t, b in zip(ts, bs)]
+        return {"entry_point": entry, "seconds": ts[k], "bytes_per_launch": bs[k],
+                "ms_per_step": ts[k] / steps * 1e3,
+                "state_updates_per_s": wl.batch * steps / ts[k],
+                "achieved_GBps": gbps[k], "frac": gbps[k] / PEAK_HBM_GBPS,
+                "region_us_per_launch": [round(t / steps * 1e6, 2) for t in ts],
+                "spread": spread(ts)}
+
+    res = {"replay": summary(*replay_regions(False, False), "replayssm_decode")}
 
     def std(i, sr_on=False):
         M.standard(i % layers, M.inputs[i % 8], sr=i if sr_on else None)
 
-    t_std = time_region(std, steps, warmup)
     std_bytes = M.standard_bytes()
-    nb = wl.batch
-    res = {
-        "replay_s": t_rep, "standard_s": t_std,
-        "replay_bytes_per_launch": rep_bytes, "standard_bytes_per_launch": std_bytes,
-        "replay_updates_per_s": nb * steps / t_rep,
-        "standard_updates_per_s": nb * steps / t_std,
-        "replay_GBps": rep_bytes * steps / t_rep / 1e9,
-        "standard_GBps": std_bytes * steps / t_std / 1e9,
-    }
-    if unordered:
-        t_pl, pl_bytes = replay_region(2 * (warmup + steps), False, ordered=False)
-        res["replay_unordered"] = {
-            "entry_point": "replayssm_decode",
-            "ms_per_step": t_pl / steps * 1e3,
-            "state_updates_per_s": nb * steps / t_pl,
-            "achieved_GBps": pl_bytes * steps / t_pl / 1e9,
-            "frac": pl_bytes * steps / t_pl / 1e9 / PEAK_HBM_GBPS,
-        }
+    ts = timed_reps(std, steps, warmup, reps)
+    res["standard"] = summary(ts, [std_bytes] * reps, "ssu_standard_decode")
+    if ordered:
+        res["replay_ordered"] = summary(*replay_regions(False, True),
+                                        "replayssm_decode_ordered")
+        res["replay_ordered"]["note"] = (
+            "host flush-first row lists, one per step phase (mod L), built by "
+            "replayssm_flush_first_order and uploaded before the timed regions")
     if sr:
-        t_rsr, rsr_bytes = replay_region(warmup + steps, True)
-        t_ssr = time_region(lambda i: std(i, True), steps, warmup)
-        res["stochastic_rounding"] = {
-            "replay_updates_per_s": nb * steps / t_rsr,
-            "replay_GBps": rsr_bytes * steps / t_rsr / 1e9,
-            "standard_updates_per_s": nb * steps / t_ssr,
-            "standard_GBps": std_bytes * steps / t_ssr / 1e9,
-        }
+        res["sr_replay"] = summary(*replay_regions(True, False), "replayssm_decode")
+        ts = timed_reps(lambda i: std(i, True), steps, warmup, reps)
+        res["sr_standard"] = summary(ts, [std_bytes] * reps, "ssu_standard_decode")
     del M
     torch.cuda.empty_cache()
     return res
 
 
-def bench_gdn(wl, layers, steps, warmup, dev):
+def bench_gdn(wl, layers, steps, warmup, dev, reps):
     import linear_recurrence_amd as R
     from workloads import TORCH_DTYPES, GdnInputs, device_normal_
     gen = GdnInputs(wl)
@@ -290,8 +316,9 @@ def bench_gdn(wl, layers, steps, warmup, dev):
     # whole ring periods per layer keep the flush share exact (lock-step rows)
     steps_r = max(layers * L, (steps // (layers * L)) * layers * L)
     warm_r = layers * L
-    t_rep = time_region(rep, steps_r, warm_r)
-    t_std = time_region(std, steps, warmup)
+    ts_rep = timed_reps(rep, steps_r, warm_r, reps)
+    ts_std = timed_reps(std, steps, warmup, reps)
+    t_rep, t_std = median(ts_rep), median(ts_std)
     sio = _sizes(io)
     tile = HV * V * K * 4
     gate = HV * K * 4 if wl.kda else HV * 4  # one entry's gates
@@ -309,6 +336,7 @@ def bench_gdn(wl, layers, steps, warmup, dev):
         "standard_GBps": per_row_std * nb * steps / t_std / 1e9,
         "replay_us_per_step": t_rep / steps_r * 1e6,
         "standard_us_per_step": t_std / steps * 1e6,
+        "replay_spread": spread(ts_rep), "standard_spread": spread(ts_std),
     }
     res["speedup"] = res["replay_updates_per_s"] / res["standard_updates_per_s"]
     del states, dr, kr, gr
@@ -316,7 +344,7 @@ def bench_gdn(wl, layers, steps, warmup, dev):
     return res
 
 
-def bench_gdn_spec(wl, T, layers, rounds, warmup, dev):
+def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps):
     """GDN speculative decoding from the ring: per round one verify of T drafts
     per row and one commit (accepted counts from a fixed seeded pattern; rows
     whose next verify would not fit fold their ring by the exact recurrence).
@@ -381,9 +409,17 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev):
     for i in range(warmup):
         rnd(i, False)
     torch.cuda.synchronize()
-    t = time_region(lambda i: rnd(warmup + i), rounds, 0)
+    ts, bs = [], []
+    for r in range(reps):
+        bytes_total[0] = 0.0
+        start = warmup + r * rounds
+        ts.append(time_region(lambda i: rnd(start + i), rounds, 0))
+        bs.append(bytes_total[0])
     for l in range(layers):
         assert np.array_equal(lay[l]["wp"].cpu().numpy(), lay[l]["w"]), "spec cursor drift"
+    k = int(np.argsort(ts)[len(ts) // 2])
+    t = ts[k]
+    bytes_total[0] = bs[k]
     acc_mean = float(np.mean([a.mean() for a in accepts]))
     res = {
         "workload": f"gdn_spec_b{nb}_hk{HK}_hv{HV}_k{K}_L{L}_T{T}",
@@ -394,17 +430,20 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev):
         "GBps": bytes_total[0] / t / 1e9, "frac": bytes_total[0] / t / 1e9 / PEAK_HBM_GBPS,
         "bytes_per_round": bytes_total[0] / rounds,
         "recurrent_verify_bytes_per_round": float(nb * HV * (1 + T) * tile),
+        "spread": spread(ts),
     }
     del lay
     torch.cuda.empty_cache()
     return res
 
 
-def _oracle_sample(wl, r0, r1, steps):
-    """The float64 oracle's replay steps for batch rows [r0, r1) over `steps`
-    steps from the workload's first (desync) warm-up step: inputs are drawn
-    here, the returned function runs the steps (single-threaded) and returns
-    its start and end times."""
+def _oracle_sample(wl, r0, r1, steps, kind="replay"):
+    """The float64 oracle on batch rows [r0, r1) over `steps` steps from the
+    workload's first (desync) warm-up step: kind "replay" runs the ReplaySSM
+    reconstruction (replay_step, the rows' own flush schedule), kind
+    "standard" the recurrence (ssu_standard_step) on the same inputs.  Inputs
+    are drawn here; the returned function runs the steps on one thread and
+    returns its start and end times."""
     from threadpoolctl import threadpool_limits
 
     from oracle import mamba2 as OM
@@ -427,11 +466,17 @@ def _oracle_sample(wl, r0, r1, steps):
     def run():
         wp = np.zeros(rows, np.int32)
         fl = np.zeros(rows, np.uint8)
+        idx = np.arange(rows)
         with threadpool_limits(1):
             t0 = time.perf_counter()
             for inp, force in seq:
+                if kind == "standard":
+                    OM.ssu_standard_step(pool, idx, inp["x"], inp["dt"], prm["A"], inp["B"],
+                                         inp["C"], D=prm["D"], z=inp["z"],
+                                         dt_bias=prm["dt_bias"], state_dtype=wl.state_dtype)
+                    continue
                 fl = fl | force
-                _, wp, fl, _ = OM.replay_step(pool, xr, dr, br, np.arange(rows), wp, fl,
+                _, wp, fl, _ = OM.replay_step(pool, xr, dr, br, idx, wp, fl,
                                               inp["x"], inp["dt"], prm["A"], inp["B"], inp["C"],
                                               D=prm["D"], z=inp["z"], dt_bias=prm["dt_bias"],
                                               state_dtype=wl.state_dtype)
@@ -439,16 +484,30 @@ def _oracle_sample(wl, r0, r1, steps):
     return run
 
 
-def cpu_baseline(wl, rows, steps):
-    """The float64 oracle's replay step on a bounded sample of the workload:
-    `rows` rows of the batch for `steps` steps, one thread; inputs drawn
-    before the clock starts."""
-    t0, t1 = _oracle_sample(wl, 0, rows, steps)()
+def host_info():
+    """Cores this process may run on, the machine's count, and the BLAS
+    thread pools numpy would use (the oracle legs limit them to one)."""
+    from threadpoolctl import threadpool_info
+    pools = [{"api": p.get("internal_api"), "threads": p.get("num_threads")}
+             for p in threadpool_info()]
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "cpu_count": os.cpu_count(),
+            "blas_pools_default": pools}
+
+
+def cpu_baseline(wl, rows, steps, kind="replay"):
+    """The float64 oracle on a bounded sample of the workload: `rows` rows of
+    the batch for `steps` steps, one thread; inputs drawn before the clock
+    starts."""
+    t0, t1 = _oracle_sample(wl, 0, rows, steps, kind)()
     dt = t1 - t0
+    what = ("ReplaySSM reconstruction (replay_step)" if kind == "replay"
+            else "standard recurrence (ssu_standard_step)")
     return {"value": rows * steps / dt, "unit": "state-updates/s", "cores": 1,
             "kind": "oracle",
-            "sample": f"float64 NumPy replay oracle, {rows} of {wl.batch} rows x {steps} "
-                      f"steps ({wl.ring_len} desync warm-up steps first), one thread, {dt:.1f} s"}
+            "sample": f"float64 NumPy {what}, {rows} of {wl.batch} rows x {steps} steps "
+                      f"({wl.ring_len} desync warm-up steps first), one thread "
+                      f"(BLAS limited to 1), {dt:.1f} s",
+            "host": host_info()}
 
 
 _SHARD_BARRIER = None
@@ -482,7 +541,8 @@ def cpu_baseline_parallel(wl, rows_per_worker, steps, workers):
     return {"value": nrows * steps / dt, "unit": "state-updates/s", "cores": workers,
             "kind": "oracle",
             "sample": f"float64 NumPy replay oracle, rows 0..{nrows - 1} of {wl.batch} x {steps} "
-                      f"steps, {workers} processes of one thread, {dt:.1f} s"}
+                      f"steps, {workers} processes of one thread, {dt:.1f} s",
+            "host": host_info()}
 
 
 def metadata_rate(rows, L, calls=2000):
@@ -510,7 +570,7 @@ def metadata_rate(rows, L, calls=2000):
 def measured_traffic(path):
     """HBM bytes per replay launch from the committed counter summary, or
     None when there is none or the kernel sources changed since it was taken."""
-    from linear_recurrence_amd.profsum import source_sha256
+    from profsum import source_sha256
     if not path or not os.path.exists(path):
         return None, "no counter summary"
     with open(path) as fh:
@@ -543,9 +603,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=512)
     ap.add_argument("--warmup", type=int, default=32)
+    ap.add_argument("--reps", type=int, default=5,
+                    help="timed regions of --steps launches per kernel (median reported)")
     ap.add_argument("--layers", type=int, default=4)
     ap.add_argument("--y-dtype", choices=("bf16", "f32"), default="bf16")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
     ap.add_argument("--no-gdn", action="store_true", help="skip the GDN measurement")
     ap.add_argument("--no-kda", action="store_true", help="skip the KDA measurement")
     ap.add_argument("--cpu-rows", type=int, default=128)
@@ -555,8 +617,8 @@ def main():
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--no-sr", action="store_true",
                     help="skip the stochastic-rounding measurement")
-    ap.add_argument("--no-unordered", action="store_true",
-                    help="skip the plain replayssm_decode region (no host row order)")
+    ap.add_argument("--no-ordered", action="store_true",
+                    help="skip replayssm_decode_ordered (host row order)")
     ap.add_argument("--no-tp", action="store_true",
                     help="skip the one-rank tensor-parallel share (10 heads)")
     args = ap.parse_args()
@@ -570,12 +632,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     from workloads import GDN, KDA, LARGE_BATCH
-    cpu = cpu_par = None
+    cpu = cpu_std = cpu_par = None
     if not args.no_cpu and not args.copy_probe:
         # CPU legs first: the parallel one forks, which must happen before
         # this process initialises the GPU
         cpu = cpu_baseline(LARGE_BATCH, args.cpu_rows, args.cpu_steps)
-        print(f"[bench] cpu oracle done: {cpu['sample']}", file=sys.stderr, flush=True)
+        print(f"[bench] cpu oracle (replay) done: {cpu['sample']}", file=sys.stderr, flush=True)
+        cpu_std = cpu_baseline(LARGE_BATCH, args.cpu_rows, args.cpu_steps, kind="standard")
+        print(f"[bench] cpu oracle (standard) done: {cpu_std['sample']}", file=sys.stderr,
+              flush=True)
         workers = min(16, len(os.sched_getaffinity(0)))
         cpu_par = cpu_baseline_parallel(LARGE_BATCH, 32, args.cpu_steps, workers)
         print(f"[bench] parallel cpu oracle done: {cpu_par['sample']}", file=sys.stderr,
@@ -588,54 +653,59 @@ def main():
         return
 
     wl = LARGE_BATCH
+    reps = max(1, args.reps)
     y_dtype = torch.bfloat16 if args.y_dtype == "bf16" else torch.float32
-    print(f"[bench] {wl.name}: layers={args.layers} steps={args.steps} warmup={args.warmup}",
-          file=sys.stderr, flush=True)
-    m = bench_mamba2(wl, args.layers, args.steps, args.warmup, y_dtype, dev, sr=not args.no_sr,
-                     unordered=not args.no_unordered)
-    print(f"[bench] mamba2 done: {m['replay_GBps']:.0f} GB/s replay, "
-          f"{m['standard_GBps']:.0f} GB/s standard", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: layers={args.layers} steps={args.steps} warmup={args.warmup} "
+          f"reps={reps}", file=sys.stderr, flush=True)
+    m = bench_mamba2(wl, args.layers, args.steps, args.warmup, y_dtype, dev, reps,
+                     sr=not args.no_sr, ordered=not args.no_ordered)
+    rp, sd = m["replay"], m["standard"]
+    print(f"[bench] mamba2 done: {rp['achieved_GBps']:.0f} GB/s replay, "
+          f"{sd['achieved_GBps']:.0f} GB/s standard", file=sys.stderr, flush=True)
     tp = None
     if not args.no_tp:
         # one tensor-parallel rank's share of the same layer: 80 / 8 = 10 heads,
         # 16 rotated layers so the working set stays far above the last-level cache
         wl_tp = dataclasses.replace(wl, name="mamba2_b512_h10_L16_bf16state_tp8share",
                                     nheads=10)
-        t = bench_mamba2(wl_tp, 16, args.steps, args.warmup, y_dtype, dev, unordered=False)
+        t = bench_mamba2(wl_tp, 16, args.steps, args.warmup, y_dtype, dev, reps,
+                         ordered=False)
         tp = {"workload": wl_tp.name, "nheads": 10, "layers_rotated": 16,
-              "replay_updates_per_s": t["replay_updates_per_s"],
-              "replay_GBps": t["replay_GBps"], "replay_frac": t["replay_GBps"] / PEAK_HBM_GBPS,
-              "standard_updates_per_s": t["standard_updates_per_s"],
-              "standard_GBps": t["standard_GBps"],
-              "speedup": t["replay_updates_per_s"] / t["standard_updates_per_s"]}
-        print(f"[bench] tp8 share done: {t['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
+              "replay_updates_per_s": t["replay"]["state_updates_per_s"],
+              "replay_GBps": t["replay"]["achieved_GBps"], "replay_frac": t["replay"]["frac"],
+              "replay_us_per_launch": t["replay"]["ms_per_step"] * 1e3,
+              "standard_updates_per_s": t["standard"]["state_updates_per_s"],
+              "standard_GBps": t["standard"]["achieved_GBps"],
+              "standard_us_per_launch": t["standard"]["ms_per_step"] * 1e3,
+              "speedup": t["replay"]["state_updates_per_s"]
+              / t["standard"]["state_updates_per_s"],
+              "spread": [t["replay"]["spread"], t["standard"]["spread"]]}
+        print(f"[bench] tp8 share done: {tp['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
               flush=True)
     gdn = None
     if not args.no_gdn:
-        gdn = bench_gdn(GDN, args.layers, args.steps, args.warmup, dev)
+        gdn = bench_gdn(GDN, args.layers, args.steps, args.warmup, dev, reps)
         print(f"[bench] gdn done: {gdn['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
               flush=True)
     kda = None
     if not args.no_kda:
-        kda = bench_gdn(KDA, args.layers, args.steps, args.warmup, dev)
+        kda = bench_gdn(KDA, args.layers, args.steps, args.warmup, dev, reps)
         print(f"[bench] kda done: {kda['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
               flush=True)
     spec = None
     if not args.no_gdn:
-        spec = bench_gdn_spec(GDN, 4, args.layers, 256, 16, dev)
+        spec = bench_gdn_spec(GDN, 4, args.layers, 256, 16, dev, reps)
         print(f"[bench] gdn spec done: {spec['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
 
-    ms_per_step = m["replay_s"] / args.steps * 1e3
-    achieved = m["replay_bytes_per_launch"] / (m["replay_s"] / args.steps) / 1e9
     traffic, traffic_note = measured_traffic(args.traffic_json)
     line = {
         "metric": METRIC,
-        "value": m["replay_updates_per_s"],
+        "value": rp["state_updates_per_s"],
         "unit": "state-updates/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": rp["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -649,31 +719,33 @@ def main():
             "y_dtype": args.y_dtype, "layers_rotated": args.layers,
             "start_positions": "uniform in [0, L)",
         },
-        "hbm_GBps": achieved,
-        "hbm_frac_of_peak": achieved / PEAK_HBM_GBPS,
+        "timing": {"regions": reps, "launches_per_region": args.steps,
+                   "reported": "median region", "events": "HIP events on the launch stream",
+                   "replay_region_us_per_launch": rp["region_us_per_launch"],
+                   "replay_spread": rp["spread"]},
+        "hbm_GBps": rp["achieved_GBps"],
+        "hbm_frac_of_peak": rp["frac"],
         "roofline": {
-            "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+            "bound": "hbm", "achieved": rp["achieved_GBps"], "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s", "frac": rp["frac"], "traffic": traffic,
             "traffic_source": traffic_note,
-            "kernel": "replayssm_decode_ordered (mamba2_decode_kernel, replay)",
-            "algorithmic_bytes_per_launch": m["replay_bytes_per_launch"],
+            "kernel": "replayssm_decode (mamba2_decode_kernel, replay)",
+            "algorithmic_bytes_per_launch": rp["bytes_per_launch"],
         },
         "cpu_baseline": cpu,
+        "cpu_baseline_standard": cpu_std,
         "cpu_baseline_parallel": cpu_par,
-        "standard": {
-            "kernel": "ssu_standard_decode",
-            "state_updates_per_s": m["standard_updates_per_s"],
-            "ms_per_step": m["standard_s"] / args.steps * 1e3,
-            "achieved_GBps": m["standard_GBps"],
-            "frac": m["standard_GBps"] / PEAK_HBM_GBPS,
-            "bytes_per_launch": m["standard_bytes_per_launch"],
-        },
-        "speedup_vs_standard": m["replay_updates_per_s"] / m["standard_updates_per_s"],
-        "replay_unordered": m.get("replay_unordered"),
+        "standard": sd,
+        "speedup_vs_standard": rp["state_updates_per_s"] / sd["state_updates_per_s"],
+        "replay_ordered": m.get("replay_ordered"),
         "gdn": gdn,
         "kda": kda,
         "gdn_spec": spec,
-        "stochastic_rounding": m.get("stochastic_rounding"),
+        "stochastic_rounding": (None if "sr_replay" not in m else {
+            "replay_updates_per_s": m["sr_replay"]["state_updates_per_s"],
+            "replay_GBps": m["sr_replay"]["achieved_GBps"],
+            "standard_updates_per_s": m["sr_standard"]["state_updates_per_s"],
+            "standard_GBps": m["sr_standard"]["achieved_GBps"]}),
         "tp8_share": tp,
         "metadata_builder": metadata_rate(wl.batch, wl.ring_len),
     }

@@ -191,9 +191,13 @@ int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring,
  * rows each of the GPU's eight dies (XCDs) takes: the positions of the list
  * are dealt to them in turn, so each takes an equal share of the flush rows,
  * first (replayssm_decode spreads them by aligned groups of 64 rows, whose
- * shares vary from step to step).  An entry outside [0, batch) is clamped
- * and sets RSSM_ST_BAD_ROW; a list that repeats a row leaves another row
- * unprocessed (its y and next cursors unspecified).  row_order == NULL:
+ * shares vary from step to step).  An entry outside [0, batch) sets
+ * RSSM_ST_BAD_ROW and its position processes nothing: the row missing from
+ * the list gets no y, no next cursors and no fold (its ring append, which
+ * does not depend on the order, still happens); every other row is
+ * processed as by replayssm_decode.  A list that repeats a row is a
+ * contract violation: that row's y, cursors and (on a flush) checkpoint are
+ * undefined, and another row is left unprocessed.  row_order == NULL:
  * RSSM_EINVAL.
  */
 int replayssm_decode_ordered(const rssm_dims* dims, void* state, void* x_ring,

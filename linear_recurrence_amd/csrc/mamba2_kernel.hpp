@@ -45,9 +45,11 @@ namespace rssm {
 // takes them first; with each aligned 64-row group taking only its own
 // flush rows, the XCDs' shares vary from step to step and the launch waits
 // for the one with the most.  The map rank -> position is a bijection for
-// any batch, so any permutation gives the same results; an entry outside
-// [0, nb) is clamped and reported as RSSM_ST_BAD_ROW.  The row order and
-// the row's metadata arrive by scalar loads.
+// any batch, so any permutation gives the same results.  An entry outside
+// [0, nb) is reported as RSSM_ST_BAD_ROW and returned as row -1: the tiles
+// at that position then write nothing (no y, cursor or state), so a bad
+// entry cannot make two workgroups fold the same checkpoint.  The row
+// order and the row's metadata arrive by scalar loads.
 typedef __attribute__((address_space(4))) const int32_t kconst_i32;
 __device__ static inline RowPick dealt_order_pick(int rank, int nb, const int32_t* row_order,
                                                   const int32_t* slot_idx,
@@ -61,10 +63,10 @@ __device__ static inline RowPick dealt_order_pick(int rank, int nb, const int32_
   for (int c = 1; c < 8; ++c)
     if (rank >= c * q + (c < m ? c : m)) x = c;
   const int pos = (rank - (x * q + (x < m ? x : m))) * 8 + x;
-  int b = *(kconst_i32*)(row_order + pos);
+  const int b = *(kconst_i32*)(row_order + pos);
   if (b < 0 || b >= nb) {
     st |= RSSM_ST_BAD_ROW;
-    b = b < 0 ? 0 : nb - 1;
+    return {-1, 0, 0, false};
   }
   return {b, *(kconst_i32*)(slot_idx + b), *(kconst_i32*)(write_pos + b), is_flush[b] != 0};
 }
@@ -422,11 +424,12 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
   } else {
     pick.s = a.slot_idx[rank];
   }
+  const bool bad_row = pick.b < 0;  // a row order entry outside the batch
   const int b = pick.b;
   const int s = pick.s;
   int w = 0;
   bool f = true;
-  if (REPLAY) {
+  if (REPLAY && !bad_row) {
     w = pick.w;
     f = pick.f;
     if (w < 0 || w >= L) {
@@ -439,10 +442,10 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
       f = true;
     }
   }
-  const bool bad_slot = s < 0 || s >= a.num_slots;
+  const bool bad_slot = !bad_row && (s < 0 || s >= a.num_slots);
   if (bad_slot) st |= RSSM_ST_BAD_SLOT;
   if (h == 0 && tid == 0) {
-    if (REPLAY) {
+    if (REPLAY && !bad_row) {
       const int nw = (f || bad_slot) ? 0 : w + 1;
       if (a.next_write_pos) a.next_write_pos[b] = nw;
       if (a.next_is_flush) a.next_is_flush[b] = (nw == L - 1) ? 1 : 0;
@@ -453,6 +456,7 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
     const int nb = gridDim.x / H;
     group_appends<IT, P, N, NT>(a, rank, nb - rank < 64 ? nb - rank : 64, h, L, tid);
   }
+  if (bad_row) return;  // the group appends above are keyed by rank, not by row
   const long yoff = ((long)b * H + h) * P;
   if (bad_slot) {
     for (int p = tid; p < P; p += NT) Elt<OT>::store1(a.y, yoff + p, __builtin_nanf(""));

@@ -394,9 +394,12 @@ __device__ static inline uint64_t swap_lane_pair(uint64_t x) {
 }
 
 // softplus(v) = log(1 + e^v): v itself above 20 (exact in fp32).  log1p(e)
-// is taken as log(u) * e / (u - 1) with u = 1 + e, which cancels the
-// rounding of u (u - 1 is exact; accurate to a few ulp with the hardware log
-// and reciprocal), and is e itself when u rounds to 1.
+// uses Kahan's compensated form, as given in D. Goldberg, "What Every
+// Computer Scientist Should Know About Floating-Point Arithmetic" (ACM
+// Computing Surveys, 1991, Theorem 4): with u = 1 + e rounded, log1p(e) =
+// log(u) * e / (u - 1), which cancels the rounding of u (u - 1 is exact;
+// accurate to a few ulp with the hardware log and reciprocal), and e itself
+// when u rounds to 1.
 __device__ static inline float softplus_f32(float v) {
   if (v > 20.f) return v;
   const float e = expf(v);

@@ -1,15 +1,15 @@
 """Summaries of rocprofv3 output for the decode kernels.
 
-    python -m linear_recurrence_amd.profsum stats RUN_kernel_stats.csv --command "..."
+    python profsum.py stats RUN_kernel_stats.csv --command "..."
         Markdown table of per-kernel launch counts and durations.
 
-    python -m linear_recurrence_amd.profsum sq RUN_counter_collection.csv --last 32
+    python profsum.py sq RUN_counter_collection.csv --last 32
         Per-kernel SQ instruction counts per wave and the VALU issue share:
         SQ_INSTS_VALU * 4 cycles (a wave64 VALU instruction on a 16-lane SIMD)
         / (1024 SIMDs * GRBM_GUI_ACTIVE / 8), GRBM_GUI_ACTIVE being summed over
         the 8 XCDs.
 
-    python -m linear_recurrence_amd.profsum traffic --fetch BENCH_FETCH.csv \
+    python profsum.py traffic --fetch BENCH_FETCH.csv \
         --write BENCH_WRITE.csv --copy-fetch COPY_FETCH.csv --copy-write COPY_WRITE.csv \
         --kernel mamba2_decode_kernel --replay --last 32 --copy-bytes 1073741824
         HBM bytes per launch of one kernel from the FETCH_SIZE and WRITE_SIZE
@@ -26,7 +26,7 @@ import json
 import os
 import sys
 
-CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "linear_recurrence_amd", "csrc")
 KERNEL_SOURCES = {
     "mamba2_decode_kernel": ("mamba2_kernel.hpp", "mamba2_decode.hip", "rssm_device.hpp",
                              "rssm_host.hpp"),

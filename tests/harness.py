@@ -320,9 +320,10 @@ def run_gdn(wl, sample, o_dtype=torch.float32, steps=None, standard=True,
             o_pool, o_dr, o_kr, o_gr, o_sl, o_wp, o_fl, ni["q"], ni["k"], ni["v"],
             ni["g"], ni["beta"], state_dtype="f32")
         assert ost == 0
-        if standard:
-            os_ref = std_ref(o_rec, o_sl, ni["q"], ni["k"], ni["v"], ni["g"], ni["beta"],
-                             state_dtype="f32")
+        # the recurrence always advances: it is also the reference for the
+        # state the GPU's checkpoint + ring represent at the end
+        os_ref = std_ref(o_rec, o_sl, ni["q"], ni["k"], ni["v"], ni["g"], ni["beta"],
+                         state_dtype="f32")
         c_wp, c_fl = OM.cursor_advance(c_wp, c_fl, L)
         if not compare:
             return
@@ -358,8 +359,18 @@ def run_gdn(wl, sample, o_dtype=torch.float32, steps=None, standard=True,
         one_step(gen.step(t), f"{wl.name} step {t}",
                  compare=(t % check_every == 0) or t == steps - 1)
     torch.cuda.synchronize()
+    # end state: the state the GPU's checkpoint + ring represent (its ring
+    # entries 0..w-1 folded by the oracle), against the recurrence; and the
+    # standard update's state
+    logical_of = OK.kda_replay_logical_state if kda else OG.gdn_replay_logical_state
+    worst["end_state"] = 0.0
     for j, r in enumerate(sample):
         s = int(slots_np[r])
+        logical = logical_of(_np(st_r[s])[None], _np(dr[s])[None], _np(kr[s])[None],
+                             _np(gr[s])[None], 0, int(c_wp[r]))
+        e = tol_state.check(f"{wl.name} row {r} GPU checkpoint+ring vs recurrence",
+                            logical, o_rec[j])
+        worst["end_state"] = max(worst["end_state"], e)
         if standard:
             tol_state.check(f"{wl.name} row {r} standard state", _np(st_s[s]), o_rec[j])
     worst["seconds"] = round(time.time() - t0, 1)

@@ -445,15 +445,41 @@ def test_row_order_gives_the_same_results(nb, H, P, N, G, L):
     torch.cuda.synchronize()
     assert torch.equal(runs["permuted"]["state"].view(torch.int16),
                        runs["plain"]["state"].view(torch.int16)), "stochastic rounding: state"
-    # an entry outside the batch is clamped and reported
-    r = fresh()
-    bad = perm.clone()
-    bad[3] = nb + 5
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    # an entry outside the batch is reported, and its position processes
+    # nothing: every other row gets exactly what the plain launch gives it,
+    # the missing row gets no y, cursor or fold (its checkpoint is untouched)
+    # and the ring appends, which do not depend on the order, all happen.
+    # Step 0 of the workload has flush rows; the missing row is one of them.
     inp = {k: v.to(dev) for k, v in gen.step(0).items()}
-    R.replayssm_decode(r["state"], r["xr"], r["dr"], r["br"], slots, r["wp"], r["fl"], inp["x"],
-                       inp["dt"], prm["A"], inp["B"], inp["C"], D=prm["D"], z=inp["z"],
-                       dt_bias=prm["dt_bias"], next_write_pos=torch.empty_like(r["wp"]),
-                       next_is_flush=torch.empty_like(r["fl"]), status=status, row_order=bad)
-    torch.cuda.synchronize()
-    assert int(status.item()) & R.ST_BAD_ROW
+    flags0 = fresh()["fl"].cpu().numpy()
+    missing_pos = int(np.nonzero(flags0[perm.cpu().numpy()])[0][0])
+    missing = int(perm[missing_pos].item())
+    bad = perm.clone()
+    bad[missing_pos] = nb + 5
+    outs = {}
+    for name, order in (("plain", None), ("bad", bad)):
+        r = fresh()
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        sentinel_wp = torch.full_like(r["wp"], -7)
+        sentinel_fl = torch.full_like(r["fl"], 7)
+        y = torch.full((nb, H, P), float("nan"), device=dev)
+        R.replayssm_decode(r["state"], r["xr"], r["dr"], r["br"], slots, r["wp"], r["fl"],
+                           inp["x"], inp["dt"], prm["A"], inp["B"], inp["C"], D=prm["D"],
+                           z=inp["z"], dt_bias=prm["dt_bias"], y=y,
+                           next_write_pos=sentinel_wp, next_is_flush=sentinel_fl,
+                           status=status, row_order=order)
+        torch.cuda.synchronize()
+        outs[name] = (r, y, sentinel_wp, sentinel_fl, int(status.item()))
+    (rp, yp, wpp, flp, stp), (rb, yb, wpb, flb, stb) = outs["plain"], outs["bad"]
+    assert stp == 0 and stb == R.ST_BAD_ROW, (stp, stb)
+    keep = torch.tensor([i for i in range(nb) if i != missing], device=dev)
+    assert torch.equal(yb[keep], yp[keep]), "bad order entry: other rows' y"
+    assert torch.isnan(yb[missing]).all(), "bad order entry: the missing row got a y"
+    assert torch.equal(wpb[keep], wpp[keep]) and torch.equal(flb[keep], flp[keep])
+    assert int(wpb[missing]) == -7 and int(flb[missing]) == 7, "missing row's cursors"
+    s_miss = int(slots[missing])
+    other = torch.tensor([i for i in range(wl.num_slots) if i != s_miss], device=dev)
+    assert torch.equal(rb["state"][other].view(torch.int16), rp["state"][other].view(torch.int16))
+    assert torch.equal(rb["state"][s_miss].cpu(), pool[s_miss]), "missing row's checkpoint"
+    for k in ("xr", "br", "dr"):
+        assert torch.equal(rb[k], rp[k]), f"bad order entry: ring {k}"
