@@ -612,6 +612,7 @@ def main():
     ap.add_argument("--no-kda", action="store_true", help="skip the KDA measurement")
     ap.add_argument("--cpu-rows", type=int, default=128)
     ap.add_argument("--cpu-steps", type=int, default=80)
+    ap.add_argument("--cpu-std-rows", type=int, default=40)
     ap.add_argument("--traffic-json", default=TRAFFIC_JSON,
                     help="per-launch HBM bytes measured with rocprofv3 counters")
     ap.add_argument("--copy-probe", action="store_true")
@@ -638,7 +639,7 @@ def main():
         # this process initialises the GPU
         cpu = cpu_baseline(LARGE_BATCH, args.cpu_rows, args.cpu_steps)
         print(f"[bench] cpu oracle (replay) done: {cpu['sample']}", file=sys.stderr, flush=True)
-        cpu_std = cpu_baseline(LARGE_BATCH, args.cpu_rows, args.cpu_steps, kind="standard")
+        cpu_std = cpu_baseline(LARGE_BATCH, args.cpu_std_rows, args.cpu_steps, kind="standard")
         print(f"[bench] cpu oracle (standard) done: {cpu_std['sample']}", file=sys.stderr,
               flush=True)
         workers = min(16, len(os.sched_getaffinity(0)))

@@ -170,7 +170,11 @@ int ssu_standard_decode(const rssm_dims* dims, void* state,
  *   next_write_pos [batch] int32 or NULL; next_is_flush [batch] uint8 or NULL
  *   x, dt, A, B, C, D, z, dt_bias, y: as for ssu_standard_decode
  *   status   int32 or NULL
- * Ring entries at positions >= write_pos are never read.
+ * Ring entries at positions >= write_pos are never read.  The order in
+ * which rows are processed does not change any result; the kernel takes the
+ * flush rows first, dealt evenly over the GPU's eight dies (XCDs) when the
+ * batch has at most 512 rows and is_flush is 8-byte aligned, otherwise by
+ * aligned groups of 64 rows.
  */
 int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring,
                      float* dt_ring, void* B_ring, const int32_t* slot_idx,
@@ -190,8 +194,9 @@ int replayssm_decode(const rssm_dims* dims, void* state, void* x_ring,
  * of replayssm_decode for any permutation; the order only decides which
  * rows each of the GPU's eight dies (XCDs) takes: the positions of the list
  * are dealt to them in turn, so each takes an equal share of the flush rows,
- * first (replayssm_decode spreads them by aligned groups of 64 rows, whose
- * shares vary from step to step).  An entry outside [0, batch) sets
+ * first (replayssm_decode does the same dealing itself for batches of up
+ * to 512 rows; a host list can also order the rows by slot).  An entry
+ * outside [0, batch) sets
  * RSSM_ST_BAD_ROW and its position processes nothing: the row missing from
  * the list gets no y, no next cursors and no fold (its ring append, which
  * does not depend on the order, still happens); every other row is

@@ -138,6 +138,9 @@ static int replay_entry(const rssm_dims* dims, void* state, void* x_ring, float*
   a.sr_seed = dims->sr_seed;
   a.sr_offset = dims->sr_offset;
   a.row_order = row_order;
+  // batches of up to 512 rows with 8-byte aligned flags: the full-grid
+  // kernel deals the flush rows over the XCDs itself
+  a.batch_dealt = dims->batch <= 512 && (reinterpret_cast<uintptr_t>(is_flush) & 7) == 0;
   return dispatch(true, a, *dims, stream);
 }
 

@@ -14,7 +14,9 @@
 // that every lane streams 16 vectors of 16 bytes (a 16 KB bf16 tile is one
 // wave).  The work is one memory round trip followed by arithmetic:
 //  * row metadata in one round trip (replay: the tile's rank picks a row,
-//    the flush rows of each 64-row group first); then every global read of
+//    flush rows first: for batches of up to 512 rows the batch's flush rows
+//    are dealt evenly over the eight XCDs, otherwise each 64-row group's
+//    flush rows come first); then every global read of
 //    the step is issued at once: the tile into registers (non-temporal), and
 //    C, z and the w+1 ring rows of x and B straight into LDS with
 //    global_load_lds (no registers, no conversion pass), and dt;
@@ -51,24 +53,85 @@ namespace rssm {
 // entry cannot make two workgroups fold the same checkpoint.  The row
 // order and the row's metadata arrive by scalar loads.
 typedef __attribute__((address_space(4))) const int32_t kconst_i32;
-__device__ static inline RowPick dealt_order_pick(int rank, int nb, const int32_t* row_order,
-                                                  const int32_t* slot_idx,
-                                                  const int32_t* write_pos,
-                                                  const uint8_t* is_flush, int& st) {
-  // ranks fill the residue classes of the positions mod 8 in turn: class x
-  // holds ranks [x*q + min(x, m), +q + (x < m)) and positions x, x+8, ...
+
+// Position in a flush-first row list dealt to the eight XCD rank ranges:
+// ranks fill the residue classes of the positions mod 8 in turn, class x
+// holding ranks [x*q + min(x, m), +q + (x < m)) and positions x, x+8, ...
+// (a bijection between ranks and positions for any batch).
+__device__ static inline int dealt_position(int rank, int nb) {
   const int q = nb >> 3, m = nb & 7;
   int x = 0;
 #pragma unroll
   for (int c = 1; c < 8; ++c)
     if (rank >= c * q + (c < m ? c : m)) x = c;
-  const int pos = (rank - (x * q + (x < m ? x : m))) * 8 + x;
+  return (rank - (x * q + (x < m ? x : m))) * 8 + x;
+}
+
+__device__ static inline RowPick dealt_order_pick(int rank, int nb, const int32_t* row_order,
+                                                  const int32_t* slot_idx,
+                                                  const int32_t* write_pos,
+                                                  const uint8_t* is_flush, int& st) {
+  const int pos = dealt_position(rank, nb);
   const int b = *(kconst_i32*)(row_order + pos);
   if (b < 0 || b >= nb) {
     st |= RSSM_ST_BAD_ROW;
     return {-1, 0, 0, false};
   }
   return {b, *(kconst_i32*)(slot_idx + b), *(kconst_i32*)(write_pos + b), is_flush[b] != 0};
+}
+
+// The same dealing without a host list, for batches of at most 512 rows:
+// every wave reads all the flush flags in one load (lane l holds rows
+// 8l..8l+7, is_flush 8-byte aligned), ballots them into eight 64-bit masks
+// and takes the row at its dealt position of the list "flush rows, then the
+// others", each enumerated by (row % 8, row / 8); the row's slot and cursor
+// follow by scalar loads.  Results do not depend on the order, so any
+// enumeration serves; this one needs no cross-lane prefix sum.
+__device__ static inline RowPick batch_dealt_pick(int rank, int nb, const int32_t* slot_idx,
+                                                  const int32_t* write_pos,
+                                                  const uint8_t* is_flush, int lane) {
+  const int pos = dealt_position(rank, nb);
+  const int r0 = 8 * lane;
+  uint64_t f8 = 0;
+  if (r0 + 8 <= nb) {
+    f8 = *reinterpret_cast<const uint64_t*>(is_flush + r0);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (r0 + k < nb && is_flush[r0 + k]) f8 |= 1ull << (8 * k);
+  }
+  uint64_t fm[8], om[8];
+  int nf = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const bool fk = ((f8 >> (8 * k)) & 0xff) != 0;
+    fm[k] = __ballot(fk);
+    om[k] = __ballot(!fk && r0 + k < nb);
+    nf += __popcll(fm[k]);
+  }
+  const bool want_flush = pos < nf;
+  int r = want_flush ? pos : pos - nf;  // rank among the rows of that kind
+  int kk = 0;
+  uint64_t msk = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint64_t mk = want_flush ? fm[k] : om[k];
+    const int c = __popcll(mk);
+    if (msk == 0) {
+      if (r < c) {
+        msk = mk;
+        kk = k;
+      } else {
+        r -= c;
+      }
+    }
+  }
+  // the lane holding the r-th set bit of msk
+  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0));
+  const uint64_t hit = __ballot(((msk >> lane) & 1) && below == r);
+  const int b = 8 * __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit)) + kk;
+  return {b, *(kconst_i32*)(slot_idx + b), *(kconst_i32*)(write_pos + b), want_flush};
 }
 
 struct Mamba2Args {
@@ -100,6 +163,7 @@ struct Mamba2Args {
   uint64_t sr_seed;    // stochastic rounding: Philox key (seed, offset)
   uint64_t sr_offset;
   const int32_t* row_order;  // flush-first row order from the host, or NULL
+  int32_t batch_dealt;       // deal the batch's flush rows in the kernel (batch_dealt_pick)
 };
 
 // Tile geometry: PER target state vectors per lane.  The replay kernel
@@ -117,7 +181,8 @@ struct TileShape {
   static constexpr int NT = NT0 < 64 ? 64 : (NT0 > 512 ? 512 : NT0);  // threads
   static constexpr int ITEMS = NVEC / NT;     // vectors per lane
   static constexpr int RPI = NT / LPR;        // state rows per item
-  // vectors per fold chunk: 32 fp32 accumulators per lane at most
+  // vectors per fold chunk: 32 fp32 accumulators per lane at most (the small
+  // replay grid halves this in the kernel, see kMinWaves)
   static constexpr int ICMAX = 32 / SV;
   static constexpr int IC = ITEMS < ICMAX ? ITEMS : ICMAX;
   static constexpr int NCH = ITEMS / IC;            // fold chunks
@@ -388,13 +453,28 @@ __device__ __forceinline__ void group_appends(const Mamba2Args& a, int g0, int n
   }
 }
 
+// Minimum waves per SIMD the compiler must fit.  A small replay grid (4
+// vectors per lane) is about one round of resident waves, so occupancy, not
+// bandwidth, bounds it: eight waves per SIMD where the registers allow it
+// without spills (bf16 state and inputs, dstate <= 128); elsewhere the
+// compiler's own choice.
+template <typename ST, typename IT, int N, bool REPLAY, int PER>
+constexpr int kMinWaves = (REPLAY && PER <= 4 && std::is_same<ST, bf16>::value &&
+                           std::is_same<IT, bf16>::value && N <= 128)
+                              ? 8
+                              : 1;
+
 template <typename ST, typename IT, typename OT, int P, int N, bool REPLAY, bool SR, int PER>
-__global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
+__global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT), (kMinWaves<ST, IT, N, REPLAY, PER>))
     mamba2_decode_kernel(const Mamba2Args a) {
   using TS = TileShape<ST, P, N, PER>;
   using SG = Stage<IT, P, N>;
   constexpr int SV = TS::SV, LPR = TS::LPR, NT = TS::NT, ITEMS = TS::ITEMS, RPI = TS::RPI;
-  constexpr int IC = TS::IC, NCH = TS::NCH;
+  // the small replay grid folds in chunks of 16 accumulators per lane, which
+  // fits its eight-waves register budget
+  constexpr int ICK = (REPLAY && PER <= 4 ? 16 : 32) / SV;
+  constexpr int IC = ITEMS < ICK ? ITEMS : ICK, NCH = ITEMS / IC;
+  static_assert(ITEMS % IC == 0, "fold chunking");
   constexpr int XV = SG::XV, BV = SG::BV;
   constexpr long kSt = sizeof(ST);
   constexpr long kIo = sizeof(IT);
@@ -419,6 +499,8 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT))
     if (a.row_order)
       pick = dealt_order_pick(rank, gridDim.x / H, a.row_order, a.slot_idx, a.write_pos,
                               a.is_flush, st);
+    else if (PER > 4 && a.batch_dealt)
+      pick = batch_dealt_pick(rank, gridDim.x / H, a.slot_idx, a.write_pos, a.is_flush, lane);
     else
       pick = flush_first_pick(rank, gridDim.x / H, a.slot_idx, a.write_pos, a.is_flush, lane);
   } else {
