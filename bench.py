@@ -4,9 +4,14 @@ Headline: Mamba2 ReplaySSM decode (replayssm_decode) at batch 512, 80 heads,
 headdim 64, dstate 128, ngroups 1, ring L = 16, bf16 inputs and bf16 state
 pool (fp32 arithmetic), start positions uniform in [0, L) so flush rows
 interleave every step.  One step = one replayssm_decode launch over the whole
-batch for one layer; ``--layers`` independent layers (state pool + rings +
-cursors each) are used round-robin so a checkpoint is re-read only after the
-other layers' ~2.7 GB have streamed (far beyond the 256 MB last-level cache).
+batch for one layer; ``--layers`` (16) independent layers (state pool + rings
++ cursors each) are used round-robin, as consecutive decode steps of a model
+with many layers would see them: between two steps of one layer the other
+layers stream ~12 GB of checkpoints and ~1.5 GB of ring and write-back
+traffic, so nothing a step reads is still in the 256 MB last-level cache.
+(With only 4 layers a layer's ring entries and freshly flushed checkpoints
+can still be cached when its next step reads them; that figure is reported
+as ``layers4_context``.)
 value = batch * steps / seconds (state-updates/s: one row advanced one step
 through one layer), from the median of ``--reps`` timed regions of exactly
 ``--steps`` launches each.
@@ -605,7 +610,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=32)
     ap.add_argument("--reps", type=int, default=5,
                     help="timed regions of --steps launches per kernel (median reported)")
-    ap.add_argument("--layers", type=int, default=4)
+    ap.add_argument("--layers", type=int, default=16,
+                    help="independent layers used round-robin (Mamba2 80 heads, GDN, KDA)")
+    ap.add_argument("--tp-layers", type=int, default=128,
+                    help="independent layers for the 10-head tensor-parallel share")
     ap.add_argument("--y-dtype", choices=("bf16", "f32"), default="bf16")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle legs")
     ap.add_argument("--no-gdn", action="store_true", help="skip the GDN measurement")
@@ -669,9 +677,9 @@ def main():
         # 16 rotated layers so the working set stays far above the last-level cache
         wl_tp = dataclasses.replace(wl, name="mamba2_b512_h10_L16_bf16state_tp8share",
                                     nheads=10)
-        t = bench_mamba2(wl_tp, 16, args.steps, args.warmup, y_dtype, dev, reps,
+        t = bench_mamba2(wl_tp, args.tp_layers, args.steps, args.warmup, y_dtype, dev, reps,
                          ordered=False)
-        tp = {"workload": wl_tp.name, "nheads": 10, "layers_rotated": 16,
+        tp = {"workload": wl_tp.name, "nheads": 10, "layers_rotated": args.tp_layers,
               "replay_updates_per_s": t["replay"]["state_updates_per_s"],
               "replay_GBps": t["replay"]["achieved_GBps"], "replay_frac": t["replay"]["frac"],
               "replay_us_per_launch": t["replay"]["ms_per_step"] * 1e3,
@@ -683,6 +691,20 @@ def main():
               "spread": [t["replay"]["spread"], t["standard"]["spread"]]}
         print(f"[bench] tp8 share done: {tp['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
               flush=True)
+    ctx4 = None
+    if args.layers != 4:
+        # the same workload over only 4 rotated layers, for comparison: there
+        # a layer's ring entries and freshly flushed checkpoints can still be
+        # in the 256 MB last-level cache when its next step reads them, which
+        # a model with many layers never sees
+        c = bench_mamba2(wl, 4, args.steps, args.warmup, y_dtype, dev, reps, ordered=False)
+        ctx4 = {"layers_rotated": 4,
+                "replay_us_per_launch": c["replay"]["ms_per_step"] * 1e3,
+                "replay_frac": c["replay"]["frac"],
+                "standard_us_per_launch": c["standard"]["ms_per_step"] * 1e3,
+                "standard_frac": c["standard"]["frac"]}
+        print(f"[bench] 4-layer context done: {ctx4['replay_us_per_launch']:.1f} us replay",
+              file=sys.stderr, flush=True)
     gdn = None
     if not args.no_gdn:
         gdn = bench_gdn(GDN, args.layers, args.steps, args.warmup, dev, reps)
@@ -748,6 +770,7 @@ def main():
             "standard_updates_per_s": m["sr_standard"]["state_updates_per_s"],
             "standard_GBps": m["sr_standard"]["achieved_GBps"]}),
         "tp8_share": tp,
+        "layers4_context": ctx4,
         "metadata_builder": metadata_rate(wl.batch, wl.ring_len),
     }
     print(json.dumps(line), flush=True)

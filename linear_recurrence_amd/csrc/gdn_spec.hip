@@ -15,15 +15,18 @@
 // Verify mapping: one workgroup per (row, value head) fp32 [V, K] tile.  q, v
 // of the T drafts, the k rows of the committed entries and of the drafts,
 // and the committed d rows are staged in LDS by direct-to-LDS loads, then
-// the tile is read once into registers.  While the tile is in flight the
-// waves form, per draft t at ring position p = w + t (one draft per wave at
-// a time), the gate products (DPP suffix products over the lanes holding
-// g_0..g_p) and the weighted dots gamma_i*(k_i.k_p), gamma_i*(k_i.q_t).
-// Then S0.k_p and S0.q_t for every state row (with bf16 inputs one matrix-core
-// product per wave, otherwise 2T butterfly row reductions), and each state
-// row walks the drafts in order, keeping the new d values in registers.
-// The drafts' (d, k, g, v, beta) are written to ring entries w..w+T-1; the
-// state and the cursor are not touched.
+// the tile is read once into registers, 1 KB contiguous per load instruction.
+// While the tile is in flight the waves form, per draft t at ring position
+// p = w + t (one draft per wave at a time), the gate products (DPP suffix
+// products over the lanes holding g_0..g_p) and the weighted dots
+// gamma_i*(k_i.k_p), gamma_i*(k_i.q_t).  Then S0.k_p and S0.q_t for every
+// state row by 2T butterfly row reductions, and each state row walks the
+// drafts in order, keeping the new d values in registers.  The drafts' d, v
+// and k rows are written to ring entries w..w+T-1 as one contiguous run per
+// array with non-temporal stores, then g and beta; the state and the cursor
+// are not touched.  (A matrix-core form of the 2T products needs the tile in
+// the operand layout, 16 state rows per load instruction, and measured
+// slower: the access pattern costs more than the products save.)
 //
 // Commit mapping: one workgroup per (row, value head); rows that do not
 // flush only advance the cursor.  Flushing tiles hold the state in fp32
@@ -67,7 +70,79 @@ struct SpecArgs {
   int32_t num_slots;
   int32_t n_draft;
   float scale;
+  int32_t fold_dealt;  // commit: deal the rows that fold over the XCDs (fold_dealt_row)
 };
+
+// Commit row of a rank, the rows that fold first, dealt evenly over the
+// eight XCD rank ranges (batches of up to 512 rows).  Only the folding
+// tiles do work, and each XCD takes its ranks in order, so without this
+// the XCD whose rows happen to fold most often sets the launch time.  Lane l
+// reads the cursor, accepted count and force flag of rows 8l..8l+7 (one
+// round trip); a row folds when w + accepted + T > L or it is forced (the
+// kernel's own rule, up to the clamping of bad counts: any rule serves, as
+// long as every wave uses the same one).  The list is "folding rows, then
+// the others", each enumerated by (row % 8, row / 8); its positions are
+// dealt to the XCDs as for the Mamba2 decode.
+__device__ static inline int fold_dealt_row(int rank, int nb, const SpecArgs& a, int lane) {
+  const int q = nb >> 3, m = nb & 7;
+  int x = 0;
+#pragma unroll
+  for (int c = 1; c < 8; ++c)
+    if (rank >= c * q + (c < m ? c : m)) x = c;
+  const int pos = (rank - (x * q + (x < m ? x : m))) * 8 + x;
+  const int r0 = 8 * lane;
+  uint32_t fb[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) fb[k] = 0;
+  if (r0 + 8 <= nb) {
+    const u32x4 w0 = ld16(a.write_pos, (long)r0 * 4), w1 = ld16(a.write_pos, (long)r0 * 4 + 16);
+    const u32x4 c0 = ld16(a.accepted, (long)r0 * 4), c1 = ld16(a.accepted, (long)r0 * 4 + 16);
+    const uint64_t f8 = a.force_flush ? *reinterpret_cast<const uint64_t*>(a.force_flush + r0) : 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int wk = (int)(k < 4 ? w0[k & 3] : w1[k & 3]);
+      const int ck = (int)(k < 4 ? c0[k & 3] : c1[k & 3]);
+      fb[k] = (wk + ck + a.n_draft > a.ring_len || ((f8 >> (8 * k)) & 0xff)) ? 1u : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      if (r0 + k < nb)
+        fb[k] = (a.write_pos[r0 + k] + a.accepted[r0 + k] + a.n_draft > a.ring_len ||
+                 (a.force_flush && a.force_flush[r0 + k]))
+                    ? 1u
+                    : 0u;
+  }
+  uint64_t fm[8], om[8];
+  int nf = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    fm[k] = __ballot(fb[k] != 0);
+    om[k] = __ballot(fb[k] == 0 && r0 + k < nb);
+    nf += __popcll(fm[k]);
+  }
+  const bool want = pos < nf;
+  int r = want ? pos : pos - nf;
+  int kk = 0;
+  uint64_t msk = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const uint64_t mk = want ? fm[k] : om[k];
+    const int c = __popcll(mk);
+    if (msk == 0) {
+      if (r < c) {
+        msk = mk;
+        kk = k;
+      } else {
+        r -= c;
+      }
+    }
+  }
+  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0));
+  const uint64_t hit = __ballot(((msk >> lane) & 1) && below == r);
+  return 8 * __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit)) + kk;
+}
 
 // Verify LDS, 16-byte chunks: [q rows 0..T-1 | v rows 0..T-1 |
 // k rows 0..L-1 (multiple of 8) | d rows 0..L-1 (fp32)]
@@ -81,19 +156,6 @@ struct VerifyStage {
   static constexpr int oK(int T) { return T * (QV + VV); }
   static constexpr int oD(int T, int L) { return oK(T) + ((L + 7) & ~7) * QV; }
   static constexpr int chunks(int T, int L) { return oD(T, L) + L * DV; }
-  // matrix-core variant: S0 . (k, q) products [V][16] fp32 after the d rows
-  static constexpr int oP(int T, int L) { return chunks(T, L); }
-  static constexpr int chunks_mfma(int T, int L) { return chunks(T, L) + V * 4; }
-};
-
-// Matrix-core split of the verify's S0 products (bf16 inputs): a wave owns
-// VBW blocks of 16 state rows by all KB blocks of 32 columns.
-template <int V, int K, int NT>
-struct VerifyMfma {
-  static constexpr int NW = NT / 64;
-  static constexpr int KB = K / 32;
-  static constexpr int VBW = V / 16 / NW;
-  static constexpr int NBLK = VBW * KB;  // blocks per wave, two 16-byte loads each
 };
 
 // 16-byte chunks [c0, c0+n) of LDS from global memory, one wave-wide
@@ -106,14 +168,10 @@ __device__ static inline void dma_rows(char* lds, int c0, int n, const char* src
   }
 }
 
-template <typename IT, typename OT, int V, int K, bool MF>
+template <typename IT, typename OT, int V, int K>
 __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_kernel(const SpecArgs a) {
   using GS = GdnShape<V, K, true>;
   using SG = VerifyStage<IT, V, K>;
-  using VM = VerifyMfma<V, K, GS::NT>;
-  static_assert(!MF || (std::is_same<IT, bf16>::value && 2 * VM::NBLK == GS::ITEMS &&
-                        VM::VBW >= 1),
-                "matrix-core verify: bf16 inputs, the tile in 16x32 blocks");
   constexpr int SV = GS::SV, LPR = GS::LPR, NT = GS::NT, ITEMS = GS::ITEMS, RPI = GS::RPI;
   constexpr int QV = SG::QV, VV = SG::VV, DV = SG::DV;
   constexpr long kIo = sizeof(IT);
@@ -180,21 +238,8 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   // runs while the tile is still in flight (the scheduling barriers keep the
   // issue order the counter wait below relies on)
   __builtin_amdgcn_sched_barrier(0);
-  if constexpr (MF) {
-    // block (vb, kb): lane l takes S0[16*vb + l%16][32*kb + 8*(l/16) .. +8],
-    // the B operand layout of the 16x16x32 product
-    const uint32_t voff = (uint32_t)(((lane & 15) * K + 8 * (lane >> 4)) * 4);
 #pragma unroll
-    for (int jb = 0; jb < VM::NBLK; ++jb) {
-      const int vb = wave * VM::VBW + jb / VM::KB, kb = jb % VM::KB;
-      const uint32_t soff = (uint32_t)((16 * vb * K + 32 * kb) * 4);
-      sv[2 * jb] = bload16_nt(trs, voff, soff);
-      sv[2 * jb + 1] = bload16_nt(trs, voff, soff + 16);
-    }
-  } else {
-#pragma unroll
-    for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
-  }
+  for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
   static_assert(ITEMS < 64, "the vmcnt field holds 6 bits");
   // everything but the ITEMS tile loads has landed: vmcnt <= ITEMS (bits 3:0
   // and 15:14 of the immediate), expcnt and lgkmcnt 0
@@ -282,55 +327,7 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
     }
   };
 
-  if constexpr (MF) {
-    // ---- 3. D[m][v] = sum_k A[m][k] S0[v][k] on the matrix cores, with
-    // A = (k_w .. k_{w+T-1}, q_0 .. q_{T-1}, zero rows) exact in bf16 and S0
-    // split into bf16 hi + lo halves (two products per block)
-    const int m = lane & 15, g4 = lane >> 4;
-    const char* arow = m < T ? Ks + (long)(w + m) * QV * 16
-                             : (m < 2 * T ? Qs + (long)(m - T) * QV * 16 : nullptr);
-    u32x4 afr[VM::KB];
-#pragma unroll
-    for (int kb = 0; kb < VM::KB; ++kb)
-      afr[kb] = arow ? *reinterpret_cast<const u32x4*>(arow + (32 * kb + 8 * g4) * 2)
-                     : u32x4{0u, 0u, 0u, 0u};
-    f32x4 acc[VM::VBW];
-#pragma unroll
-    for (int j = 0; j < VM::VBW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int jb = 0; jb < VM::NBLK; ++jb) {
-      float f[8];
-      Elt<float>::unpack(sv[2 * jb], f);
-      Elt<float>::unpack(sv[2 * jb + 1], f + 4);
-      u32x4 hi, lo;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t h = bf16_pair(f[2 * q], f[2 * q + 1]);
-        hi[q] = h;
-        lo[q] = bf16_pair(f[2 * q] - __uint_as_float(h << 16),
-                          f[2 * q + 1] - __uint_as_float(h & 0xffff0000u));
-      }
-      const int j = jb / VM::KB, kb = jb % VM::KB;
-      acc[j] = mfma16x16x32_bf16(afr[kb], hi, acc[j]);
-      acc[j] = mfma16x16x32_bf16(afr[kb], lo, acc[j]);
-    }
-    // lane holds D[4*g4 + r][16*vb + m]: products of state row v in P[v][.]
-    float* Pm = reinterpret_cast<float*>(lds + (long)SG::oP(T, L) * 16);
-#pragma unroll
-    for (int j = 0; j < VM::VBW; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Pm[(16 * (wave * VM::VBW + j) + m) * 16 + 4 * g4 + r] = acc[j][r];
-    __syncthreads();
-    for (int vr = tid; vr < V; vr += NT) {
-      float pkv[kMaxDraft], pqv[kMaxDraft];
-#pragma unroll
-      for (int t = 0; t < kMaxDraft; ++t) {
-        pkv[t] = t < T ? Pm[vr * 16 + t] : 0.f;
-        pqv[t] = t < T ? Pm[vr * 16 + T + t] : 0.f;
-      }
-      draft_row(vr, pkv, pqv, true);
-    }
-  } else {
+  {
     // ---- 3. S0 . k_{w+t} and S0 . q_t for this lane's state rows
     const int c = tid % LPR;
     const int prow = tid / LPR;
@@ -378,25 +375,27 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   }
   __syncthreads();  // the drafts' d rows are in LDS
 
-  // ---- 5. ring entries w..w+T-1: d, k (one writer per key head), g, v, beta
+  // ---- 5. ring entries w..w+T-1 of d, v and k (one writer per key head):
+  // each array's T rows are one contiguous run in the ring, written by
+  // consecutive lanes with non-temporal stores (written this way, scattered
+  // ring writes inside the tile read stream cost a third of the per-row
+  // layout); then g and beta
   const bool k_writer = (hv % a.vpk) == 0;
-  for (int e = tid; e < T * (DV + QV + VV); e += NT) {
-    const int t = e / (DV + QV + VV);
-    const int r = e - t * (DV + QV + VV);
-    const int p = w + t;
-    if (r < DV) {
-      const u32x4 x = *reinterpret_cast<const u32x4*>(lds + ((long)oD + p * DV + r) * 16);
-      st16(a.d_ring, (dring0 + (long)p * V) * 4 + r * 16, x);
-    } else if (r < DV + QV) {
-      if (k_writer) {
-        const int cc = r - DV;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(Ks + ((long)p * QV + cc) * 16);
-        st16(a.k_ring, (kring0 + (long)p * K) * kIo + cc * 16, x);
+  {
+    const int nd = T * DV, nv = T * VV, nk = k_writer ? T * QV : 0;
+    for (int e = tid; e < nd + nv + nk; e += NT) {
+      if (e < nd) {
+        const u32x4 x = *reinterpret_cast<const u32x4*>(lds + ((long)oD + w * DV + e) * 16);
+        st16_stream(a.d_ring, (dring0 + (long)w * V) * 4 + (long)e * 16, x);
+      } else if (e < nd + nv) {
+        const int u = e - nd;  // draft rows t = u / VV, staged contiguously
+        const u32x4 x = *reinterpret_cast<const u32x4*>(Vs + (long)u * 16);
+        st16_stream(a.v_ring, (dring0 + (long)w * V) * kIo + (long)u * 16, x);
+      } else {
+        const int u = e - nd - nv;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(Ks + ((long)w * QV + u) * 16);
+        st16_stream(a.k_ring, (kring0 + (long)w * K) * kIo + (long)u * 16, x);
       }
-    } else {
-      const int cc = r - DV - QV;
-      const u32x4 x = *reinterpret_cast<const u32x4*>(Vs + ((long)t * VV + cc) * 16);
-      st16(a.v_ring, (dring0 + (long)p * V) * kIo + cc * 16, x);
     }
   }
   if (wave == 0) {
@@ -428,12 +427,22 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_ke
   extern __shared__ __attribute__((aligned(16))) char lds[];
   const int HV = a.v_heads, HK = a.k_heads, T = a.n_draft, L = a.ring_len;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int b = tile / HV;
-  const int hv = tile - b * HV;
+  const int rank = tile / HV;
+  const int hv = tile - rank * HV;
   const int hk = hv / a.vpk;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int b = rank;
+  if (a.fold_dealt) {
+    __shared__ int row_of_rank;
+    if (wave == 0) {
+      const int r = fold_dealt_row(rank, gridDim.x / HV, a, lane);
+      if (lane == 0) row_of_rank = r;
+    }
+    __syncthreads();
+    b = row_of_rank;
+  }
 
   const int s = a.slot_idx[b];
   const int acc = a.accepted[b];
@@ -517,25 +526,15 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_ke
     st16_stream(tptr, (long)lane_off + it * NT * 16, Elt<float>::pack(S[it]));
 }
 
-// bf16 inputs take the matrix-core products when their LDS fits; otherwise
-// (fp32 inputs, or the largest rings) the vector path.
 template <typename IT, typename OT, int V, int K>
 static int launch_verify(const SpecArgs& a, int batch, hipStream_t stream) {
   using SG = VerifyStage<IT, V, K>;
   constexpr int NT = GdnShape<V, K, true>::NT;
   const size_t fixed = (2 * kMaxDraft * 64 + kMaxDraft) * sizeof(float);
   const unsigned grid = (unsigned)((long)batch * a.v_heads);
-  if constexpr (std::is_same<IT, bf16>::value &&
-                2 * VerifyMfma<V, K, NT>::NBLK == GdnShape<V, K, true>::ITEMS) {
-    const size_t lds = (size_t)SG::chunks_mfma(a.n_draft, a.ring_len) * 16;
-    if (lds + fixed <= kMaxLds)
-      return launch_kernel(
-          reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, true>), grid, NT,
-          lds, stream, a);
-  }
   const size_t lds = (size_t)SG::chunks(a.n_draft, a.ring_len) * 16;
   if (lds + fixed > kMaxLds) return RSSM_ESHAPE;  // staged rows must fit one workgroup's LDS
-  return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, false>),
+  return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K>),
                        grid, NT, lds, stream, a);
 }
 
@@ -665,6 +664,11 @@ extern "C" int replayssm_gdn_spec_commit(const rssm_gdn_dims* dims, int32_t n_dr
   a.next_write_pos = next_write_pos;
   a.flushed = flushed;
   a.status = status;
+  // batches of up to 512 rows with 16-byte aligned cursors and counts (and
+  // 8-byte aligned force flags): the kernel deals the folding rows over the
+  // XCDs itself
+  a.fold_dealt = dims->batch <= 512 && aligned16(write_pos) && aligned16(accepted) &&
+                 (!force_flush || (reinterpret_cast<uintptr_t>(force_flush) & 7) == 0);
   switch (dims->io_dtype) {
     case RSSM_F32: return commit_shape<float>(a, *dims, stream);
     case RSSM_BF16: return commit_shape<bf16>(a, *dims, stream);
