@@ -630,6 +630,8 @@ def main():
                     help="skip replayssm_decode_ordered (host row order)")
     ap.add_argument("--no-tp", action="store_true",
                     help="skip the one-rank tensor-parallel share (10 heads)")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the 4-layer comparison run of the headline workload")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -692,7 +694,7 @@ def main():
         print(f"[bench] tp8 share done: {tp['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
               flush=True)
     ctx4 = None
-    if args.layers != 4:
+    if args.layers != 4 and not args.no_context:
         # the same workload over only 4 rotated layers, for comparison: there
         # a layer's ring entries and freshly flushed checkpoints can still be
         # in the 256 MB last-level cache when its next step reads them, which

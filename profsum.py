@@ -11,10 +11,13 @@
 
     python profsum.py traffic --fetch BENCH_FETCH.csv \
         --write BENCH_WRITE.csv --copy-fetch COPY_FETCH.csv --copy-write COPY_WRITE.csv \
-        --kernel mamba2_decode_kernel --replay --last 32 --copy-bytes 1073741824
+        --kernel mamba2_decode_kernel --replay --last 32 --copy-bytes 1073741824 \
+        [--ea-rd BENCH_EA_RD.csv --ea-wr BENCH_EA_WR.csv]
         HBM bytes per launch of one kernel from the FETCH_SIZE and WRITE_SIZE
         counters (KiB per dispatch), each scaled by the ratio between the known
-        size of a plain device copy and what the same counter reads for it.
+        size of a plain device copy and what the same counter reads for it;
+        with the --ea-* runs, the same bytes counted a second way, from the
+        L2-to-fabric request counters by request size (no scaling).
         Prints JSON; ``source_sha256`` fingerprints the kernel sources the
         counters were taken on, so a reader can tell when they are stale.
 """
@@ -70,6 +73,45 @@ def _dispatch_kib(path, kernel, replay, last):
     if not ids:
         raise SystemExit(f"no dispatches of {kernel} (replay={replay}) in {path}")
     return [per[i] for i in ids]
+
+
+def _dispatch_counters(path, kernel, replay, last):
+    """{counter: value} per dispatch of `kernel` (summed over instances), the last `last`."""
+    per = {}
+    for r in _rows(path):
+        name = r["Kernel_Name"]
+        if kernel not in name or _is_replay(name) != replay:
+            continue
+        c = per.setdefault(int(r["Dispatch_Id"]), {})
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)[-last:] if last else sorted(per)
+    if not ids:
+        raise SystemExit(f"no dispatches of {kernel} (replay={replay}) in {path}")
+    return [per[i] for i in ids]
+
+
+def ea_bytes(rd_path, wr_path, kernel, replay, last):
+    """HBM-side bytes per dispatch from the L2-to-fabric request counters,
+    each request counted at its size: reads 32 B x RDREQ_32B + 64 B x
+    RDREQ_64B + 128 B x RDREQ_128B, writes 64 B x WRREQ_64B + 32 B x the
+    other write requests.  No copy-kernel scaling is involved."""
+    rd = _dispatch_counters(rd_path, kernel, replay, last)
+    wr = _dispatch_counters(wr_path, kernel, replay, last)
+    n = len(rd)
+    g = lambda lst, k: sum(c.get(k, 0.0) for c in lst) / len(lst)
+    r32, r64, r128 = (g(rd, "TCC_EA0_RDREQ_32B_sum"), g(rd, "TCC_EA0_RDREQ_64B_sum"),
+                      g(rd, "TCC_EA0_RDREQ_128B_sum"))
+    rall = g(rd, "TCC_EA0_RDREQ_sum")
+    w64, wall = g(wr, "TCC_EA0_WRREQ_64B_sum"), g(wr, "TCC_EA0_WRREQ_sum")
+    return {
+        "dispatches": [n, len(wr)],
+        "rdreq_per_dispatch": {"all": rall, "32B": r32, "64B": r64, "128B": r128},
+        "wrreq_per_dispatch": {"all": wall, "64B": w64},
+        "rdreq_dram_per_dispatch": g(wr, "TCC_EA0_RDREQ_DRAM_sum"),
+        "wrreq_dram_per_dispatch": g(wr, "TCC_EA0_WRREQ_DRAM_sum"),
+        "read_bytes_per_launch": 32 * r32 + 64 * r64 + 128 * r128,
+        "write_bytes_per_launch": 64 * w64 + 32 * (wall - w64),
+    }
 
 
 def _copy_factor(path, known_bytes):
@@ -148,6 +190,10 @@ def cmd_traffic(args):
         "bytes_per_launch": fb + wb,
         "source_sha256": source_sha256(args.kernel),
     }
+    if args.ea_rd and args.ea_wr:
+        ea = ea_bytes(args.ea_rd, args.ea_wr, args.kernel, args.replay, args.last)
+        ea["bytes_per_launch"] = ea["read_bytes_per_launch"] + ea["write_bytes_per_launch"]
+        res["ea_request_counters"] = ea
     if args.command:
         res["commands"] = args.command
     print(json.dumps(res, indent=1))
@@ -172,6 +218,10 @@ def main(argv=None):
     t.add_argument("--replay", action="store_true")
     t.add_argument("--last", type=int, default=0)
     t.add_argument("--copy-bytes", type=float, default=float(1 << 30))
+    t.add_argument("--ea-rd", default=None,
+                   help="counter CSV with TCC_EA0_RDREQ{,_32B,_64B,_128B}_sum")
+    t.add_argument("--ea-wr", default=None,
+                   help="counter CSV with TCC_EA0_WRREQ{,_64B}_sum (and the _DRAM pair)")
     t.add_argument("--command", action="append", default=None)
     args = ap.parse_args(argv)
     {"stats": cmd_stats, "sq": cmd_sq, "traffic": cmd_traffic}[args.mode](args)
