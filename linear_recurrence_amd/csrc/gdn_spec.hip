@@ -158,6 +158,17 @@ struct VerifyStage {
   static constexpr int chunks(int T, int L) { return oD(T, L) + L * DV; }
 };
 
+// Matrix-core form of the verify's 2T products (bf16 inputs, V = K = 128,
+// 256 threads): each wave owns 32 state rows of the contiguously loaded tile
+// (rows it*8 + 2*wave + h) and a private LDS region, first the staging
+// buffer of one 16-row x 32-column block (row pitch 36 floats against bank
+// conflicts), then its rows' products [32][16].
+struct VerifyMfma {
+  static constexpr int kPitch = 36;
+  static constexpr int kRegionFloats = 16 * kPitch;  // >= 32 * 16
+  static constexpr size_t kBytes = 4 * kRegionFloats * sizeof(float);
+};
+
 // 16-byte chunks [c0, c0+n) of LDS from global memory, one wave-wide
 // direct-to-LDS load per 64 chunks; chunk u comes from src + 16*u.
 __device__ static inline void dma_rows(char* lds, int c0, int n, const char* src, int wave,
@@ -168,10 +179,12 @@ __device__ static inline void dma_rows(char* lds, int c0, int n, const char* src
   }
 }
 
-template <typename IT, typename OT, int V, int K>
+template <typename IT, typename OT, int V, int K, bool MF>
 __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_kernel(const SpecArgs a) {
   using GS = GdnShape<V, K, true>;
   using SG = VerifyStage<IT, V, K>;
+  static_assert(!MF || (std::is_same<IT, bf16>::value && V == 128 && K == 128 && GS::NT == 256),
+                "matrix-core products: bf16 inputs, V = K = 128, four waves");
   constexpr int SV = GS::SV, LPR = GS::LPR, NT = GS::NT, ITEMS = GS::ITEMS, RPI = GS::RPI;
   constexpr int QV = SG::QV, VV = SG::VV, DV = SG::DV;
   constexpr long kIo = sizeof(IT);
@@ -327,7 +340,71 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
     }
   };
 
-  {
+  if constexpr (MF) {
+    // ---- 3. D[m][row] = sum_k A[m][k] S0[row][k] on the matrix cores, A =
+    // (k_w .. k_{w+T-1}, q_0 .. q_{T-1}, zero rows) exact in bf16, S0 split
+    // into bf16 hi + lo halves (two products per block).  A wave's block of
+    // 16 rows x 32 columns goes through its LDS region into the B operand
+    // layout (lane l: row l%16, columns 8*(l/16) ..+8) while the tile loads
+    // stay 1 KB contiguous per instruction.
+    float* const Wb = reinterpret_cast<float*>(lds + (long)SG::chunks(T, L) * 16) +
+                      wave * VerifyMfma::kRegionFloats;
+    constexpr int PI = VerifyMfma::kPitch;
+    const int h = lane >> 5, q32 = lane & 31;  // this lane's row of the pair, 16-byte column
+    const int m = lane & 15, g4 = lane >> 4;   // operand row / column group
+    const char* arow = m < T ? Ks + (long)(w + m) * QV * 16
+                             : (m < 2 * T ? Qs + (long)(m - T) * QV * 16 : nullptr);
+    f32x4 acc[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      acc[b2] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        if ((q32 >> 3) == kb) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            *reinterpret_cast<u32x4*>(Wb + (2 * i + h) * PI + 4 * (q32 & 7)) = sv[8 * b2 + i];
+        }
+        __builtin_amdgcn_wave_barrier();
+        const float* src = Wb + m * PI + 8 * g4;
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = src[e];
+        u32x4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t hb = bf16_pair(f[2 * e], f[2 * e + 1]);
+          hi[e] = hb;
+          lo[e] = bf16_pair(f[2 * e] - __uint_as_float(hb << 16),
+                            f[2 * e + 1] - __uint_as_float(hb & 0xffff0000u));
+        }
+        const u32x4 afr = arow ? *reinterpret_cast<const u32x4*>(arow + (32 * kb + 8 * g4) * 2)
+                               : u32x4{0u, 0u, 0u, 0u};
+        acc[b2] = mfma16x16x32_bf16(afr, hi, acc[b2]);
+        acc[b2] = mfma16x16x32_bf16(afr, lo, acc[b2]);
+        __builtin_amdgcn_wave_barrier();
+      }
+    }
+    // lane holds products 4*g4 + r of the wave's local row 16*b2 + m
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Wb[(16 * b2 + m) * 16 + 4 * g4 + r] = acc[b2][r];
+    __syncthreads();
+    for (int vr = tid; vr < V; vr += NT) {
+      // row vr = it*8 + 2*w' + h' lives in wave w' as local row 2*it + h'
+      const float* Pr = reinterpret_cast<const float*>(lds + (long)SG::chunks(T, L) * 16) +
+                        ((vr & 7) >> 1) * VerifyMfma::kRegionFloats +
+                        (2 * (vr >> 3) + (vr & 1)) * 16;
+      float pkv[kMaxDraft], pqv[kMaxDraft];
+#pragma unroll
+      for (int t = 0; t < kMaxDraft; ++t) {
+        pkv[t] = t < T ? Pr[t] : 0.f;
+        pqv[t] = t < T ? Pr[T + t] : 0.f;
+      }
+      draft_row(vr, pkv, pqv, true);
+    }
+  } else {
     // ---- 3. S0 . k_{w+t} and S0 . q_t for this lane's state rows
     const int c = tid % LPR;
     const int prow = tid / LPR;
@@ -526,6 +603,9 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_ke
     st16_stream(tptr, (long)lane_off + it * NT * 16, Elt<float>::pack(S[it]));
 }
 
+// bf16 inputs at V = K = 128 take the matrix-core products when the extra
+// LDS fits; otherwise (fp32 inputs, other shapes, the largest rings) the
+// vector path.
 template <typename IT, typename OT, int V, int K>
 static int launch_verify(const SpecArgs& a, int batch, hipStream_t stream) {
   using SG = VerifyStage<IT, V, K>;
@@ -533,8 +613,14 @@ static int launch_verify(const SpecArgs& a, int batch, hipStream_t stream) {
   const size_t fixed = (2 * kMaxDraft * 64 + kMaxDraft) * sizeof(float);
   const unsigned grid = (unsigned)((long)batch * a.v_heads);
   const size_t lds = (size_t)SG::chunks(a.n_draft, a.ring_len) * 16;
+  if constexpr (std::is_same<IT, bf16>::value && V == 128 && K == 128 && NT == 256) {
+    if (lds + VerifyMfma::kBytes + fixed <= kMaxLds)
+      return launch_kernel(
+          reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, true>), grid, NT,
+          lds + VerifyMfma::kBytes, stream, a);
+  }
   if (lds + fixed > kMaxLds) return RSSM_ESHAPE;  // staged rows must fit one workgroup's LDS
-  return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K>),
+  return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, false>),
                        grid, NT, lds, stream, a);
 }
 
