@@ -24,8 +24,12 @@ def _unit(rng, shape):
     return a / np.linalg.norm(a, axis=-1, keepdims=True)
 
 
-def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32):
-    print(f"case: spec nb={nb} HK={HK} HV={HV} K={K} V={V} L={L} T={T} io={io}", flush=True)
+def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32, offset=0):
+    """offset > 0 places the cursors and accepted counts `offset` int32s past
+    a 16-byte boundary, which turns the commit's own dealing of the folding
+    rows off."""
+    print(f"case: spec nb={nb} HK={HK} HV={HV} K={K} V={V} L={L} T={T} io={io} "
+          f"offset={offset}", flush=True)
     rng = np.random.default_rng(seed)
     dev = torch.device("cuda:0")
     ns = nb + 3
@@ -37,8 +41,9 @@ def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32
     gr = torch.full((ns, HV, L), float("nan"), device=dev)
     vr = torch.full((ns, HV, L, V), float("nan"), dtype=io, device=dev)
     br = torch.full((ns, HV, L), float("nan"), device=dev)
-    wp = torch.zeros(nb, dtype=torch.int32, device=dev)
-    nwp = torch.empty_like(wp)
+    wp = torch.zeros(nb + offset, dtype=torch.int32, device=dev)[offset:]
+    nwp = torch.zeros(nb + offset, dtype=torch.int32, device=dev)[offset:]
+    acc_buf = torch.zeros(nb + offset, dtype=torch.int32, device=dev)
     fl = torch.empty(nb, dtype=torch.uint8, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     sl = torch.tensor(slots, device=dev)
@@ -76,7 +81,9 @@ def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32
             assert (d <= bound).all(), f"round {r}: o error {d.max():.2e}"
         acc = rng.integers(0, T + 1, nb).astype(np.int32)
         force = (rng.random(nb) < 0.1).astype(np.uint8)
-        R.replayssm_gdn_spec_commit(st, kr, gr, vr, br, sl, wp, torch.tensor(acc, device=dev),
+        acc_t = acc_buf[offset:]
+        acc_t.copy_(torch.tensor(acc, device=dev))
+        R.replayssm_gdn_spec_commit(st, kr, gr, vr, br, sl, wp, acc_t,
                                     T, nwp, force_flush=torch.tensor(force, device=dev),
                                     flushed=fl, status=status)
         o_wp, o_fl, ost = OS.gdn_spec_commit(o_pool, *o_rings[1:], o_sl, o_wp, acc[sample], T,
@@ -116,6 +123,13 @@ def test_spec_full_size_bf16_output():
     """256 rows, 16 key / 32 value heads, K = V = 128, L = 16, 4 drafts."""
     run_spec(256, 16, 32, 128, 128, 16, 4, torch.bfloat16, 12, [0, 99, 200, 255], seed=4,
              out=torch.bfloat16)
+
+
+def test_spec_commit_without_its_own_dealing():
+    """The commit's fallback order (rows in batch order): a batch over 512
+    rows, and cursors / accepted counts off a 16-byte boundary."""
+    run_spec(520, 1, 2, 64, 64, 8, 3, torch.bfloat16, 8, [0, 255, 300, 519], seed=91)
+    run_spec(40, 2, 4, 128, 128, 16, 4, torch.bfloat16, 10, range(0, 40, 7), seed=92, offset=1)
 
 
 def test_spec_bad_cursor_is_refused():

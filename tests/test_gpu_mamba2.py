@@ -117,12 +117,77 @@ def test_large_batch_full_size_bench_configuration():
 
 
 def test_flush_first_row_order_with_a_ragged_row_group():
-    """Replay tiles visit the flush rows of each 64-row group first; 110 rows
-    (a full group and a ragged one of 46) with uniform start positions: every
-    row is still advanced exactly once per step (all cursors bit-exact) and
-    sampled rows on both sides of the group boundary match the oracle."""
+    """Replay tiles visit the flush rows first, dealt over the XCDs by the
+    kernel (110 rows: the last lane of the flag load holds a ragged 6 rows)
+    with uniform start positions: every row is still advanced exactly once
+    per step (all cursors bit-exact) and sampled rows across the batch match
+    the oracle."""
     wl = LARGE_BATCH.with_batch(110, steps=40, num_slots=256, name="mamba2_b110_desync")
     run_mamba2(wl, sample=[0, 37, 63, 64, 90, 109], y_dtype=torch.float32)
+
+
+def test_batch_over_512_rows_takes_the_per_group_order():
+    """600 rows x 16 heads (a full grid of one-wave tiles): past 512 rows the
+    kernel takes each aligned 64-row group's flush rows first instead of
+    dealing the batch's; all cursors bit-exact, sampled rows in the first,
+    a middle and the ragged last group against the oracle."""
+    print("case: batch 600, 16 heads, per-group flush order", flush=True)
+    wl = Mamba2Workload("mamba2_b600_h16", 600, 16, 64, 128, 1, 16, 35, 1200, "bf16", "bf16",
+                        2950, desync=True)
+    run_mamba2(wl, sample=[0, 63, 64, 300, 575, 576, 599], y_dtype=torch.float32,
+               standard=False)
+
+
+def test_unaligned_flush_flags_give_the_same_results():
+    """Flush flags at an odd byte address turn the kernel's own dealing off
+    (it reads the flags 8 bytes at a time); the rows are then taken per
+    64-row group, and y, checkpoints, rings and cursors stay bit for bit
+    those of the aligned launch."""
+    import linear_recurrence_amd as R
+    from workloads import TORCH_DTYPES
+    print("case: unaligned flush flags, 130 rows x 64 heads", flush=True)
+    dev = torch.device("cuda:0")
+    nb, H, P, N, G, L = 130, 64, 64, 128, 1, 16
+    wl = Mamba2Workload("unaligned_flags", nb, H, P, N, G, L, 2 * L + 3, 2 * nb + 8, "bf16",
+                        "bf16", 2960, desync=True)
+    gen = Mamba2Inputs(wl)
+    prm = {k: v.to(dev) for k, v in gen.params().items()}
+    slots = gen.slot_idx().to(dev)
+    iot = TORCH_DTYPES["bf16"]
+    pool = gen.state_pool(gen.slot_idx().tolist())
+    runs = {}
+    for name, off in (("aligned", 0), ("unaligned", 1)):
+        ns = wl.num_slots
+        fl_a = torch.zeros(nb + 1, dtype=torch.uint8, device=dev)[off:off + nb]
+        fl_b = torch.zeros(nb + 1, dtype=torch.uint8, device=dev)[off:off + nb]
+        assert (fl_a.data_ptr() % 8 == 0) == (off == 0)
+        fl_a.copy_((gen.start_positions() == L - 1).to(torch.uint8).to(dev))
+        runs[name] = {"state": pool.clone().to(dev),
+                      "xr": torch.zeros((ns, H, L, P), dtype=iot, device=dev),
+                      "dr": torch.zeros((ns, H, L), device=dev),
+                      "br": torch.zeros((ns, G, L, N), dtype=iot, device=dev),
+                      "wp": gen.start_positions().to(dev), "nwp": torch.empty(nb, dtype=torch.int32,
+                                                                              device=dev),
+                      "fl": fl_a, "nfl": fl_b, "ys": []}
+    for t in range(wl.steps):
+        inp = {k: v.to(dev) for k, v in gen.step(t).items()}
+        for r in runs.values():
+            y = R.replayssm_decode(r["state"], r["xr"], r["dr"], r["br"], slots, r["wp"], r["fl"],
+                                   inp["x"], inp["dt"], prm["A"], inp["B"], inp["C"], D=prm["D"],
+                                   z=inp["z"], dt_bias=prm["dt_bias"], next_write_pos=r["nwp"],
+                                   next_is_flush=r["nfl"])
+            r["ys"].append(y.clone())
+            r["wp"], r["nwp"] = r["nwp"], r["wp"]
+            r["fl"], r["nfl"] = r["nfl"], r["fl"]
+    torch.cuda.synchronize()
+    a, u = runs["aligned"], runs["unaligned"]
+    for t in range(wl.steps):
+        assert torch.equal(a["ys"][t].view(torch.int16), u["ys"][t].view(torch.int16)), f"y {t}"
+    for k in ("state", "xr", "br"):
+        assert torch.equal(a[k].view(torch.int16), u[k].view(torch.int16)), k
+    assert torch.equal(a["dr"].view(torch.int32), u["dr"].view(torch.int32))
+    assert torch.equal(a["wp"], u["wp"]) and torch.equal(a["fl"], u["fl"])
+    log(f"{wl.steps} steps: unaligned flags give the aligned launch's results bit for bit")
 
 
 def test_large_batch_full_size_fp32_output():
