@@ -350,7 +350,9 @@ int replayssm_gdn_spec_verify(const rssm_gdn_dims* dims, int32_t n_draft,
  * would not fit) or force_flush[b] != 0 (force_flush may be NULL), the state
  * is rebuilt by the recurrence over entries 0..w'-1 from their raw inputs,
  *     S = g_i*S;  d = beta_i*(v_i - S@k_i);  S += outer(d, k_i),
- * stored, and w' = 0.  Writes next_write_pos[b] = w' (must not alias
+ * stored, and w' = 0 (fp32 arithmetic; the decays are carried as one running
+ * product and applied to the state at the end, or earlier when that product
+ * leaves [2^-60, 2^60]: the same recurrence up to rounding).  Writes next_write_pos[b] = w' (must not alias
  * write_pos) and flushed[b] (may be NULL).  accepted outside [0, T] sets
  * RSSM_ST_RING_OVERFLOW and is clamped.
  */

@@ -28,11 +28,19 @@
 // the operand layout, 16 state rows per load instruction, and measured
 // slower: the access pattern costs more than the products save.)
 //
-// Commit mapping: one workgroup per (row, value head); rows that do not
-// flush only advance the cursor.  Flushing tiles hold the state in fp32
-// registers and apply the recurrence entry by entry (scale by g, row dots
-// with k by butterfly reduction, d passed within the wave through LDS,
-// rank-1 update; the waves never wait for one another), then store it.
+// Commit mapping: only about one row in L/(mean acceptance) folds per round,
+// so the commit is a small grid working through a task list (batches of up
+// to 512 rows): each workgroup reads every row's cursor, accepted count,
+// force flag and slot in one round trip and lists the folding rows in LDS;
+// workgroup 0 writes the cursor outputs; the (folding row, value head) tasks
+// are shared out over the grid, the same count to every XCD.  Larger batches
+// take one workgroup per (row, value head).  A fold holds the tile in fp32
+// registers, eight lanes per state row (128-byte segments per load), and
+// applies the recurrence entry by entry in order: the decays are carried as
+// one running product instead of scaling every element, the row dots with k
+// are sums over eight lanes by DPP, d passes within the wave through LDS,
+// then the rank-1 update (the waves never wait for one another); the tile is
+// stored scaled by the product.
 #include <math.h>
 
 #include "gdn_common.hpp"
@@ -70,79 +78,35 @@ struct SpecArgs {
   int32_t num_slots;
   int32_t n_draft;
   float scale;
-  int32_t fold_dealt;  // commit: deal the rows that fold over the XCDs (fold_dealt_row)
+  int32_t fold_tasks;  // commit: a small grid working through a list of fold tasks
+  int32_t n_rows;      // commit: batch rows
 };
 
-// Commit row of a rank, the rows that fold first, dealt evenly over the
-// eight XCD rank ranges (batches of up to 512 rows).  Only the folding
-// tiles do work, and each XCD takes its ranks in order, so without this
-// the XCD whose rows happen to fold most often sets the launch time.  Lane l
-// reads the cursor, accepted count and force flag of rows 8l..8l+7 (one
-// round trip); a row folds when w + accepted + T > L or it is forced (the
-// kernel's own rule, up to the clamping of bad counts: any rule serves, as
-// long as every wave uses the same one).  The list is "folding rows, then
-// the others", each enumerated by (row % 8, row / 8); its positions are
-// dealt to the XCDs as for the Mamba2 decode.
-__device__ static inline int fold_dealt_row(int rank, int nb, const SpecArgs& a, int lane) {
-  const int q = nb >> 3, m = nb & 7;
-  int x = 0;
-#pragma unroll
-  for (int c = 1; c < 8; ++c)
-    if (rank >= c * q + (c < m ? c : m)) x = c;
-  const int pos = (rank - (x * q + (x < m ? x : m))) * 8 + x;
-  const int r0 = 8 * lane;
-  uint32_t fb[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) fb[k] = 0;
-  if (r0 + 8 <= nb) {
-    const u32x4 w0 = ld16(a.write_pos, (long)r0 * 4), w1 = ld16(a.write_pos, (long)r0 * 4 + 16);
-    const u32x4 c0 = ld16(a.accepted, (long)r0 * 4), c1 = ld16(a.accepted, (long)r0 * 4 + 16);
-    const uint64_t f8 = a.force_flush ? *reinterpret_cast<const uint64_t*>(a.force_flush + r0) : 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int wk = (int)(k < 4 ? w0[k & 3] : w1[k & 3]);
-      const int ck = (int)(k < 4 ? c0[k & 3] : c1[k & 3]);
-      fb[k] = (wk + ck + a.n_draft > a.ring_len || ((f8 >> (8 * k)) & 0xff)) ? 1u : 0u;
-    }
-  } else {
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (r0 + k < nb)
-        fb[k] = (a.write_pos[r0 + k] + a.accepted[r0 + k] + a.n_draft > a.ring_len ||
-                 (a.force_flush && a.force_flush[r0 + k]))
-                    ? 1u
-                    : 0u;
+// Commit decision of one row: the cursor after its accepted drafts (clamped
+// to the ring, with the status bit, when the counts are bad), whether the
+// row folds its ring into the checkpoint, and its status bits.  Both the
+// cursor outputs and the fold work follow this one rule.
+struct CommitRow {
+  int wn;
+  int st;
+  bool flush;
+};
+__device__ static inline CommitRow commit_row(int s, int w, int acc, bool force,
+                                              const SpecArgs& a) {
+  const int T = a.n_draft, L = a.ring_len;
+  int wn = (int)((uint32_t)w + (uint32_t)acc);
+  int st = 0;
+  if (acc < 0 || acc > T || wn < 0 || wn > L) {
+    st |= RSSM_ST_RING_OVERFLOW;
+    wn = wn < 0 ? 0 : (wn > L ? L : wn);
   }
-  uint64_t fm[8], om[8];
-  int nf = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    fm[k] = __ballot(fb[k] != 0);
-    om[k] = __ballot(fb[k] == 0 && r0 + k < nb);
-    nf += __popcll(fm[k]);
-  }
-  const bool want = pos < nf;
-  int r = want ? pos : pos - nf;
-  int kk = 0;
-  uint64_t msk = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint64_t mk = want ? fm[k] : om[k];
-    const int c = __popcll(mk);
-    if (msk == 0) {
-      if (r < c) {
-        msk = mk;
-        kk = k;
-      } else {
-        r -= c;
-      }
-    }
-  }
-  const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(msk >> 32),
-                                              __builtin_amdgcn_mbcnt_lo((uint32_t)msk, 0));
-  const uint64_t hit = __ballot(((msk >> lane) & 1) && below == r);
-  return 8 * __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit)) + kk;
+  const bool bad_slot = s < 0 || s >= a.num_slots;
+  if (bad_slot) st |= RSSM_ST_BAD_SLOT;
+  return {wn, st, !bad_slot && (wn + T > L || force)};
 }
+
+// Largest batch the task-list commit takes (one row list in LDS).
+constexpr int kTaskRows = 512;
 
 // Verify LDS, 16-byte chunks: [q rows 0..T-1 | v rows 0..T-1 |
 // k rows 0..L-1 (multiple of 8) | d rows 0..L-1 (fp32)]
@@ -481,126 +445,287 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   }
 }
 
-// Commit LDS, 16-byte chunks: [k rows 0..L-1 | v rows 0..L-1]; then 2*V
+// Commit LDS: [k rows 0..L-1 as fp32 | v rows 0..L-1 as stored]; then 2*V
 // floats for the d of the step in flight (double buffered).
 template <typename IT, int V, int K>
 struct CommitStage {
-  static constexpr int IV = Elt<IT>::kPer16;
-  static constexpr int QV = K / IV;
-  static constexpr int VV = V / IV;
-  static constexpr int oV(int L) { return L * QV; }
-  static constexpr size_t bytes(int L) { return (size_t)L * (QV + VV) * 16 + 2 * V * 4; }
+  static constexpr int VV = V / Elt<IT>::kPer16;  // 16-byte chunks of a v row
+  static constexpr size_t oV(int L) { return (size_t)L * K * 4; }
+  static constexpr size_t oD(int L) { return oV(L) + (size_t)L * V * sizeof(IT); }
+  static constexpr size_t bytes(int L) { return oD(L) + 2 * V * 4; }
 };
 
-template <typename IT, int V, int K>
-__global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_kernel(const SpecArgs a) {
-  using GS = GdnShape<V, K, true>;  // 256 threads: half the waves of the 512-thread shape
-  using SG = CommitStage<IT, V, K>;
-  constexpr int SV = GS::SV, LPR = GS::LPR, NT = GS::NT, ITEMS = GS::ITEMS, RPI = GS::RPI;
-  constexpr int QV = SG::QV, VV = SG::VV;
-  constexpr long kIo = sizeof(IT);
-  using RR = RowReduce<ITEMS, LPR>;
+// Lanes of a fold tile: lane m of the eight lanes of group g holds 16 bytes
+// of each of the NSEG 128-byte segments of RPL state rows (rows
+// wave*RPW + 8*rr + g), so each load or store instruction moves eight whole
+// 128-byte segments and a row's dot with k is a sum over eight lanes.
+template <int V, int K, int NT>
+struct FoldLayout {
+  static constexpr int NSEG = K / 32;
+  static constexpr int ITEMS = V * K / 4 / NT;
+  static constexpr int RPL = ITEMS / NSEG;
+  static constexpr int RPW = 8 * RPL;
+  static_assert(RPW * (NT / 64) == V && RPL * NSEG == ITEMS, "fold tile layout");
+};
 
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int HV = a.v_heads, HK = a.k_heads, T = a.n_draft, L = a.ring_len;
-  const int tile = xcd_tile(blockIdx.x, gridDim.x);
-  const int rank = tile / HV;
-  const int hv = tile - rank * HV;
+// Sums of RPL per-lane partials over the eight lanes of each group, folded:
+// every level halves the partials a lane keeps (partners: mirror within the
+// 8 lanes, then lane xor 2, lane xor 1, all by DPP), so lane m ends with the
+// total of partial item(m), held by DUP lanes.
+template <int RPL>
+struct Reduce8 {
+  static constexpr int LV = RPL >= 8 ? 3 : (RPL >= 4 ? 2 : (RPL >= 2 ? 1 : 0));
+  static constexpr int DUP = 8 >> LV;
+  template <int O>
+  __device__ static inline float partner(float x) {
+    constexpr int ctrl = O == 4 ? 0x141 : (O == 2 ? 0x4E : 0xB1);  // half-row mirror, quad perms
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
+  }
+  template <int LVL>
+  __device__ static inline void level(float (&v)[RPL], int m) {
+    if constexpr (LVL < 3) {
+      constexpr int O = 4 >> LVL;
+      if constexpr (LVL < LV) {
+        constexpr int h = (RPL >> LVL) >> 1;
+        const bool up = (m & O) != 0;
+#pragma unroll
+        for (int j = 0; j < h; ++j) {
+          const float send = up ? v[j] : v[j + h];
+          const float keep = up ? v[j + h] : v[j];
+          v[j] = keep + partner<O>(send);
+        }
+      } else {
+        v[0] += partner<O>(v[0]);
+      }
+      level<LVL + 1>(v, m);
+    }
+  }
+  __device__ static inline void run(float (&v)[RPL], int m) { level<0>(v, m); }
+  __device__ static inline int item(int m) {
+    int it = 0;
+    if (LV > 0 && (m & 4)) it += RPL / 2;
+    if (LV > 1 && (m & 2)) it += RPL / 4;
+    if (LV > 2 && (m & 1)) it += RPL / 8;
+    return it;
+  }
+};
+
+// The fold holds the tile as gam * S: a step's decay g multiplies the scalar
+// gam instead of every element, the row dot is gam * (S.k) and the rank-1
+// update adds (d / gam) k to S.  Algebraically the recurrence; when gam
+// would leave [2^-60, 2^60] (or g is 0 or not finite) the pending decay and
+// the step's own are applied to S element by element and gam restarts at 1.
+constexpr float kLazyFloor = 0x1p-60f, kLazyCeil = 0x1p60f;
+
+// Exact fold of one (slot, value head) tile: the recurrence over ring entries
+// 0..wn-1 from their raw inputs, in order, the state held in fp32 registers.
+// Every thread of the workgroup calls it; the staged rows go to `stage`.
+template <typename IT, int V, int K>
+__device__ static inline void fold_tile(const SpecArgs& a, int s, int hv, int wn, char* stage,
+                                        int tid) {
+  using GS = GdnShape<V, K, true>;
+  using FL = FoldLayout<V, K, GS::NT>;
+  using SG = CommitStage<IT, V, K>;
+  using RD = Reduce8<FL::RPL>;
+  constexpr int NT = GS::NT, ITEMS = FL::ITEMS, NSEG = FL::NSEG, RPL = FL::RPL, RPW = FL::RPW;
+  constexpr int EPV = Elt<IT>::kPer16;
+  constexpr long kIo = sizeof(IT);
+  const int HV = a.v_heads, HK = a.k_heads, L = a.ring_len;
   const int hk = hv / a.vpk;
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int b = rank;
-  if (a.fold_dealt) {
-    __shared__ int row_of_rank;
-    if (wave == 0) {
-      const int r = fold_dealt_row(rank, gridDim.x / HV, a, lane);
-      if (lane == 0) row_of_rank = r;
-    }
-    __syncthreads();
-    b = row_of_rank;
-  }
+  const int m = lane & 7;
+  const int row0 = wave * RPW + (lane >> 3);  // this lane's rows: row0 + 8*rr
 
-  const int s = a.slot_idx[b];
-  const int acc = a.accepted[b];
-  int wn = a.write_pos[b] + acc;
-  int st = 0;
-  if (acc < 0 || acc > T || wn < 0 || wn > L) {
-    st |= RSSM_ST_RING_OVERFLOW;
-    wn = wn < 0 ? 0 : (wn > L ? L : wn);
-  }
-  const bool bad_slot = s < 0 || s >= a.num_slots;
-  if (bad_slot) st |= RSSM_ST_BAD_SLOT;
-  const bool flush = !bad_slot && (wn + T > L || (a.force_flush && a.force_flush[b]));
-  if (hv == 0 && tid == 0) {
-    if (a.next_write_pos) a.next_write_pos[b] = flush ? 0 : wn;
-    if (a.flushed) a.flushed[b] = flush ? 1 : 0;
-    if (st && a.status) atomicOr(a.status, st);
-  }
-  if (!flush || wn == 0) return;
-
-  // ---- exact fold: the recurrence over entries 0..wn-1 from their raw inputs
   char* const tptr = (char*)a.state + ((long)s * HV + hv) * (long)V * K * 4;
   const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(V * K * 4));
-  const uint32_t lane_off = tid * 16;
+  const uint32_t voff = (uint32_t)(row0 * K * 4 + m * 16);
   u32x4 sv[ITEMS];
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it) sv[it] = bload16_nt(trs, lane_off, it * NT * 16);
+  for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg)
+      sv[rr * NSEG + sg] = bload16_nt(trs, voff, rr * 8 * K * 4 + sg * 128);
   const long kring0 = ((long)s * HK + hk) * (long)L * K;
   const long vring0 = ((long)s * HV + hv) * (long)L * V;
   const long gring0 = ((long)s * HV + hv) * L;
-  dma_rows(lds, 0, wn * QV, (const char*)a.k_ring + kring0 * kIo, wave, lane, NT);
-  dma_rows(lds, SG::oV(L), wn * VV, (const char*)a.v_ring + vring0 * kIo, wave, lane, NT);
+  // k rows 0..wn-1 to LDS as fp32 (one 16-byte vector of the ring per step of
+  // this loop), v rows as stored
+  float* const K32 = reinterpret_cast<float*>(stage);
+  for (int e = tid; e < wn * K / EPV; e += NT) {
+    float f[EPV];
+    Elt<IT>::unpack(ld16(a.k_ring, (kring0 + (long)e * EPV) * kIo), f);
+#pragma unroll
+    for (int q = 0; q < EPV; q += 4)
+      *reinterpret_cast<u32x4*>(K32 + (long)e * EPV + q) = Elt<float>::pack(f + q);
+  }
+  dma_rows(stage, (int)(SG::oV(L) / 16), wn * SG::VV, (const char*)a.v_ring + vring0 * kIo,
+           wave, lane, NT);
   const float gl = lane < wn ? a.g_ring[gring0 + lane] : 1.f;
   const float bl = lane < wn ? a.beta_ring[gring0 + lane] : 0.f;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const char* Ks = lds;
-  const char* Vs = lds + (long)SG::oV(L) * 16;
-  float* dbuf = reinterpret_cast<float*>(lds + (size_t)L * (QV + VV) * 16);
+  const char* Vs = stage + SG::oV(L);
+  float* const dbuf = reinterpret_cast<float*>(stage + SG::oD(L));
 
-  const int c = tid % LPR;
-  const int prow = tid / LPR;
-  float S[ITEMS][SV];
+  float S[RPL][NSEG * 4];
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it) Elt<float>::unpack(sv[it], S[it]);
-  const bool writer = (c % RR::DUP) == 0;
+  for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg) Elt<float>::unpack(sv[rr * NSEG + sg], &S[rr][sg * 4]);
+  const int my_row = row0 + 8 * RD::item(m);  // the row whose total this lane ends with
+  const bool writer = (m % RD::DUP) == 0;
+  float gam = 1.f;
   for (int i = 0; i < wn; ++i) {
     const float gi = lane_value(gl, i), bi = lane_value(bl, i);
-    float kseg[SV];
-    LdsRead<IT>::template seg<SV>(Ks + (long)i * QV * 16, c * SV, kseg);
-    float part[ITEMS];
+    float gn = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gam * gi)));
+    if (!(gn >= kLazyFloor && gn <= kLazyCeil)) {
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
+      for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+        for (int e = 0; e < NSEG * 4; ++e) S[rr][e] = (S[rr][e] * gam) * gi;
+      gn = 1.f;
+    }
+    float kv[NSEG * 4];
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg)
+      Elt<float>::unpack(*reinterpret_cast<const u32x4*>(K32 + (long)i * K + sg * 32 + m * 4),
+                         &kv[sg * 4]);
+    float part[RPL];
+#pragma unroll
+    for (int rr = 0; rr < RPL; ++rr) {
       float x = 0.f;
 #pragma unroll
-      for (int j = 0; j < SV; ++j) {
-        S[it][j] *= gi;
-        x = fmaf(S[it][j], kseg[j], x);
-      }
-      part[it] = x;
+      for (int e = 0; e < NSEG * 4; ++e) x = fmaf(S[rr][e], kv[e], x);
+      part[rr] = x;
     }
-    RR::run(part, tid);
+    RD::run(part, m);
+    const float rinv = 1.f / gn;
     float* db = dbuf + (i & 1) * V;
-#pragma unroll
-    for (int j = 0; j < RR::NF; ++j) {
-      const int vr = RR::item(j, tid) * RPI + prow;
-      if (writer) db[vr] = bi * (LdsRead<IT>::one(Vs + (long)i * VV * 16, vr) - part[j]);
+    if (writer) {
+      const float vr = LdsRead<IT>::one(Vs + (long)i * V * kIo, my_row);
+      db[my_row] = (bi * fmaf(-gn, part[0], vr)) * rinv;
     }
     // the d values of a wave's state rows come from that wave's own lanes
     // (a row's lanes never span two waves) and one wave's LDS operations
     // complete in order, so no workgroup barrier is needed here
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int it = 0; it < ITEMS; ++it) {
-      const float dv = db[it * RPI + prow];
+    for (int rr = 0; rr < RPL; ++rr) {
+      const float dv = db[row0 + 8 * rr];
 #pragma unroll
-      for (int j = 0; j < SV; ++j) S[it][j] = fmaf(dv, kseg[j], S[it][j]);
+      for (int e = 0; e < NSEG * 4; ++e) S[rr][e] = fmaf(dv, kv[e], S[rr][e]);
     }
+    gam = gn;
   }
 #pragma unroll
-  for (int it = 0; it < ITEMS; ++it)
-    st16_stream(tptr, (long)lane_off + it * NT * 16, Elt<float>::pack(S[it]));
+  for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg) {
+      float o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = S[rr][sg * 4 + e] * gam;
+      st16_stream(tptr, (long)voff + rr * 8 * K * 4 + sg * 128, Elt<float>::pack(o));
+    }
+}
+
+template <typename IT, int V, int K>
+__global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_kernel(const SpecArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char lds[];
+  const int HV = a.v_heads;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  if (!a.fold_tasks) {
+    // one workgroup per (row, value head), rows in batch order
+    const int tile = xcd_tile(blockIdx.x, gridDim.x);
+    const int b = tile / HV;
+    const int hv = tile - b * HV;
+    const int s = a.slot_idx[b];
+    const CommitRow cr = commit_row(s, a.write_pos[b], a.accepted[b],
+                                    a.force_flush && a.force_flush[b], a);
+    if (hv == 0 && tid == 0) {
+      if (a.next_write_pos) a.next_write_pos[b] = cr.flush ? 0 : cr.wn;
+      if (a.flushed) a.flushed[b] = cr.flush ? 1 : 0;
+      if (cr.st && a.status) atomicOr(a.status, cr.st);
+    }
+    if (cr.flush && cr.wn > 0) fold_tile<IT, V, K>(a, s, hv, cr.wn, lds, tid);
+    return;
+  }
+
+  // Task list: wave 0 reads every row's (slot, cursor, accepted, force) in one
+  // round trip, lane l rows 8l..8l+7, and lists the folding rows' slot and
+  // cursor in LDS; workgroup 0 also writes every row's cursor outputs.  The
+  // fold tasks (folding row f, value head hv), f-major, are taken by
+  // workgroups j, j + P, ... of the P-workgroup grid; with P a multiple of 8
+  // each XCD receives the same share of them.
+  __shared__ int fold_slot[kTaskRows];
+  __shared__ uint8_t fold_wn[kTaskRows];
+  __shared__ int fold_count;
+  const int nb = a.n_rows;
+  if (wave == 0) {
+    const int r0 = 8 * lane;
+    // every load before any store (the outputs could alias the inputs as far
+    // as the compiler knows), so the rows cost one round trip
+    // (without force flags the flag loads read bytes of slot_idx, in bounds
+    // for every row, and are masked off: no load sits behind a branch)
+    const bool has_force = a.force_flush != nullptr;
+    const uint8_t* const fsrc =
+        has_force ? a.force_flush : reinterpret_cast<const uint8_t*>(a.slot_idx);
+    int sk[8], wk[8], ak[8], fk[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = r0 + k < nb ? r0 + k : nb - 1;
+      sk[k] = a.slot_idx[r];
+      wk[k] = a.write_pos[r];
+      ak[k] = a.accepted[r];
+      fk[k] = fsrc[r];
+    }
+    bool fb[8];
+    int st = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int r = r0 + k;
+      fb[k] = false;
+      if (r < nb) {
+        const CommitRow cr = commit_row(sk[k], wk[k], ak[k], has_force && fk[k] != 0, a);
+        fb[k] = cr.flush && cr.wn > 0;
+        wk[k] = cr.wn;
+        st |= cr.st;
+        if (blockIdx.x == 0) {
+          if (a.next_write_pos) a.next_write_pos[r] = cr.flush ? 0 : cr.wn;
+          if (a.flushed) a.flushed[r] = cr.flush ? 1 : 0;
+        }
+      }
+    }
+    int base = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint64_t m = __ballot(fb[k]);
+      if (fb[k]) {
+        const int f = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        fold_slot[f] = sk[k];
+        fold_wn[f] = (uint8_t)wk[k];
+      }
+      base += __popcll(m);
+    }
+    if (lane == 0) fold_count = base;
+    if (blockIdx.x == 0 && a.status && __ballot(st != 0)) {
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) st |= __shfl_xor(st, o, 64);
+      if (lane == 0) atomicOr(a.status, st);
+    }
+  }
+  __syncthreads();
+  const int ntask = fold_count * HV;
+  for (int t = blockIdx.x; t < ntask; t += gridDim.x) {
+    const int f = t / HV;
+    const int hv = t - f * HV;
+    if (t != (int)blockIdx.x) __syncthreads();  // every wave is done with the staged rows
+    fold_tile<IT, V, K>(a, fold_slot[f], hv, fold_wn[f], lds, tid);
+  }
 }
 
 // bf16 inputs at V = K = 128 take the matrix-core products when the extra
@@ -624,13 +749,18 @@ static int launch_verify(const SpecArgs& a, int batch, hipStream_t stream) {
                        grid, NT, lds, stream, a);
 }
 
+// Grid of the task-list commit: enough resident workgroups to keep every CU
+// busy with the folds of a typical round, a multiple of 8 (one share per XCD).
+constexpr long kCommitGrid = 1024;
+
 template <typename IT, int V, int K>
 static int launch_commit(const SpecArgs& a, int batch, hipStream_t stream) {
   const size_t lds = CommitStage<IT, V, K>::bytes(a.ring_len);
   if (lds > kMaxLds) return RSSM_ESHAPE;
+  const long tiles = (long)batch * a.v_heads;
+  const long grid = a.fold_tasks ? (tiles < kCommitGrid ? tiles : kCommitGrid) : tiles;
   return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_commit_kernel<IT, V, K>),
-                       (unsigned)((long)batch * a.v_heads), GdnShape<V, K, true>::NT, lds, stream,
-                       a);
+                       (unsigned)grid, GdnShape<V, K, true>::NT, lds, stream, a);
 }
 
 template <typename IT, typename OT>
@@ -750,11 +880,10 @@ extern "C" int replayssm_gdn_spec_commit(const rssm_gdn_dims* dims, int32_t n_dr
   a.next_write_pos = next_write_pos;
   a.flushed = flushed;
   a.status = status;
-  // batches of up to 512 rows with 16-byte aligned cursors and counts (and
-  // 8-byte aligned force flags): the kernel deals the folding rows over the
-  // XCDs itself
-  a.fold_dealt = dims->batch <= 512 && aligned16(write_pos) && aligned16(accepted) &&
-                 (!force_flush || (reinterpret_cast<uintptr_t>(force_flush) & 7) == 0);
+  // batches of up to kTaskRows rows: a small grid works through the list of
+  // fold tasks; larger batches: one workgroup per (row, value head)
+  a.n_rows = dims->batch;
+  a.fold_tasks = dims->batch <= kTaskRows;
   switch (dims->io_dtype) {
     case RSSM_F32: return commit_shape<float>(a, *dims, stream);
     case RSSM_BF16: return commit_shape<bf16>(a, *dims, stream);

@@ -24,10 +24,11 @@ def _unit(rng, shape):
     return a / np.linalg.norm(a, axis=-1, keepdims=True)
 
 
-def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32, offset=0):
-    """offset > 0 places the cursors and accepted counts `offset` int32s past
-    a 16-byte boundary, which turns the commit's own dealing of the folding
-    rows off."""
+def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32, offset=0,
+             gates=None):
+    """offset > 0 places the cursors and accepted counts `offset` int32s off
+    a 16-byte boundary.  gates(rng, shape) draws the decays g (default:
+    exp(-softplus(N(0, 1)))))."""
     print(f"case: spec nb={nb} HK={HK} HV={HV} K={K} V={V} L={L} T={T} io={io} "
           f"offset={offset}", flush=True)
     rng = np.random.default_rng(seed)
@@ -61,8 +62,9 @@ def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32
         q = torch.tensor(_unit(rng, (nb, T, HK, K)), dtype=io, device=dev)
         k = torch.tensor(_unit(rng, (nb, T, HK, K)), dtype=io, device=dev)
         v = torch.tensor(rng.normal(size=(nb, T, HV, V)), dtype=io, device=dev)
-        g = torch.tensor(np.exp(-np.log1p(np.exp(rng.normal(size=(nb, T, HV))))),
-                         dtype=torch.float32, device=dev)
+        gv = (gates(rng, (nb, T, HV)) if gates else
+              np.exp(-np.log1p(np.exp(rng.normal(size=(nb, T, HV))))))
+        g = torch.tensor(gv, dtype=torch.float32, device=dev)
         beta = torch.tensor(1 / (1 + np.exp(-rng.normal(size=(nb, T, HV)))),
                             dtype=torch.float32, device=dev)
         o = R.replayssm_gdn_spec_verify(st, dr, kr, gr, vr, br, sl, wp, q, k, v, g, beta,
@@ -125,9 +127,34 @@ def test_spec_full_size_bf16_output():
              out=torch.bfloat16)
 
 
-def test_spec_commit_without_its_own_dealing():
-    """The commit's fallback order (rows in batch order): a batch over 512
-    rows, and cursors / accepted counts off a 16-byte boundary."""
+def _extreme_gates(rng, shape):
+    """Decays that drive the fold's running decay product out of its lazy
+    range within a few entries: zeros, 1e-9, 1e-30 and ones among the usual
+    draws."""
+    g = np.exp(-np.log1p(np.exp(rng.normal(size=shape))))
+    pick = rng.random(shape)
+    g = np.where(pick < 0.1, 0.0, g)
+    g = np.where((pick >= 0.1) & (pick < 0.2), 1e-9, g)
+    g = np.where((pick >= 0.2) & (pick < 0.25), 1e-30, g)
+    return np.where((pick >= 0.25) & (pick < 0.35), 1.0, g)
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_spec_fold_with_extreme_decays(io):
+    """Decays of 0, 1e-9 and 1e-30 (and 1) in the folded entries, long rings
+    (L = 64 with bf16 inputs, 48 with fp32, whose verify staging would not
+    fit one workgroup's LDS at 64) and L = 16: the fold keeps the decay of
+    the tile as one running product and applies it to the state whenever
+    that product leaves [2^-60, 2^60]."""
+    L = 64 if io == torch.bfloat16 else 48
+    run_spec(6, 2, 4, 128, 128, L, 8, io, 24, range(6), seed=95, gates=_extreme_gates)
+    run_spec(6, 1, 2, 64, 128, 16, 4, io, 16, range(6), seed=96, gates=_extreme_gates)
+
+
+def test_spec_commit_large_batch_and_unaligned_cursors():
+    """A batch over 512 rows takes the commit's grid of one workgroup per
+    (row, value head); cursors and accepted counts off a 16-byte boundary
+    (the task-list commit reads them element by element)."""
     run_spec(520, 1, 2, 64, 64, 8, 3, torch.bfloat16, 8, [0, 255, 300, 519], seed=91)
     run_spec(40, 2, 4, 128, 128, 16, 4, torch.bfloat16, 10, range(0, 40, 7), seed=92, offset=1)
 
