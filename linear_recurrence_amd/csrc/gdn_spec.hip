@@ -517,62 +517,21 @@ struct Reduce8 {
 // the step's own are applied to S element by element and gam restarts at 1.
 constexpr float kLazyFloor = 0x1p-60f, kLazyCeil = 0x1p60f;
 
-// Exact fold of one (slot, value head) tile: the recurrence over ring entries
-// 0..wn-1 from their raw inputs, in order, the state held in fp32 registers.
-// Every thread of the workgroup calls it; the staged rows go to `stage`.
-template <typename IT, int V, int K>
-__device__ static inline void fold_tile(const SpecArgs& a, int s, int hv, int wn, char* stage,
-                                        int tid) {
-  using GS = GdnShape<V, K, true>;
-  using FL = FoldLayout<V, K, GS::NT>;
-  using SG = CommitStage<IT, V, K>;
-  using RD = Reduce8<FL::RPL>;
-  constexpr int NT = GS::NT, ITEMS = FL::ITEMS, NSEG = FL::NSEG, RPL = FL::RPL, RPW = FL::RPW;
-  constexpr int EPV = Elt<IT>::kPer16;
+// The entry loop of a fold: this lane's rows S of the tile, entries 0..wn-1
+// in order (k rows as fp32 in K32, v rows as stored in Vs, g and beta of
+// entry i in lane i of gl, bl), the result left in S.
+template <typename IT, int V, int K, int NT, int RPL, int E>
+__device__ static inline void fold_steps(float (&S)[RPL][E], const float* K32, const char* Vs,
+                                         float* dbuf, float gl, float bl, int wn, int tid) {
+  using FL = FoldLayout<V, K, NT>;
+  using RD = Reduce8<RPL>;
+  static_assert(RPL == FL::RPL && E == FL::NSEG * 4, "fold registers");
+  constexpr int NSEG = FL::NSEG, RPW = FL::RPW;
   constexpr long kIo = sizeof(IT);
-  const int HV = a.v_heads, HK = a.k_heads, L = a.ring_len;
-  const int hk = hv / a.vpk;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 7;
-  const int row0 = wave * RPW + (lane >> 3);  // this lane's rows: row0 + 8*rr
-
-  char* const tptr = (char*)a.state + ((long)s * HV + hv) * (long)V * K * 4;
-  const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(V * K * 4));
-  const uint32_t voff = (uint32_t)(row0 * K * 4 + m * 16);
-  u32x4 sv[ITEMS];
-#pragma unroll
-  for (int rr = 0; rr < RPL; ++rr)
-#pragma unroll
-    for (int sg = 0; sg < NSEG; ++sg)
-      sv[rr * NSEG + sg] = bload16_nt(trs, voff, rr * 8 * K * 4 + sg * 128);
-  const long kring0 = ((long)s * HK + hk) * (long)L * K;
-  const long vring0 = ((long)s * HV + hv) * (long)L * V;
-  const long gring0 = ((long)s * HV + hv) * L;
-  // k rows 0..wn-1 to LDS as fp32 (one 16-byte vector of the ring per step of
-  // this loop), v rows as stored
-  float* const K32 = reinterpret_cast<float*>(stage);
-  for (int e = tid; e < wn * K / EPV; e += NT) {
-    float f[EPV];
-    Elt<IT>::unpack(ld16(a.k_ring, (kring0 + (long)e * EPV) * kIo), f);
-#pragma unroll
-    for (int q = 0; q < EPV; q += 4)
-      *reinterpret_cast<u32x4*>(K32 + (long)e * EPV + q) = Elt<float>::pack(f + q);
-  }
-  dma_rows(stage, (int)(SG::oV(L) / 16), wn * SG::VV, (const char*)a.v_ring + vring0 * kIo,
-           wave, lane, NT);
-  const float gl = lane < wn ? a.g_ring[gring0 + lane] : 1.f;
-  const float bl = lane < wn ? a.beta_ring[gring0 + lane] : 0.f;
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  const char* Vs = stage + SG::oV(L);
-  float* const dbuf = reinterpret_cast<float*>(stage + SG::oD(L));
-
-  float S[RPL][NSEG * 4];
-#pragma unroll
-  for (int rr = 0; rr < RPL; ++rr)
-#pragma unroll
-    for (int sg = 0; sg < NSEG; ++sg) Elt<float>::unpack(sv[rr * NSEG + sg], &S[rr][sg * 4]);
+  const int row0 = wave * RPW + (lane >> 3);
   const int my_row = row0 + 8 * RD::item(m);  // the row whose total this lane ends with
   const bool writer = (m % RD::DUP) == 0;
   float gam = 1.f;
@@ -621,12 +580,101 @@ __device__ static inline void fold_tile(const SpecArgs& a, int s, int hv, int wn
 #pragma unroll
   for (int rr = 0; rr < RPL; ++rr)
 #pragma unroll
-    for (int sg = 0; sg < NSEG; ++sg) {
-      float o[4];
+    for (int e = 0; e < NSEG * 4; ++e) S[rr][e] *= gam;
+}
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations are outstanding and leaves the other counters alone.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// Barrier for LDS only: this wave's LDS operations complete, s_barrier, then
+// an acquire fence so that no LDS access moves above it (the release fence
+// of __syncthreads() would also wait for the tile loads still in flight).
+__device__ static inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(63) & ~(15 << 8));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Exact fold of one (slot, value head) tile: the recurrence over ring entries
+// 0..wn-1 from their raw inputs, in order, the state held in fp32 registers.
+// Every thread of the workgroup calls it; the staged rows go to `stage`.
+template <typename IT, int V, int K>
+__device__ static inline void fold_tile(const SpecArgs& a, int s, int hv, int wn, char* stage,
+                                        int tid) {
+  using GS = GdnShape<V, K, true>;
+  using FL = FoldLayout<V, K, GS::NT>;
+  using SG = CommitStage<IT, V, K>;
+  constexpr int NT = GS::NT, ITEMS = FL::ITEMS, NSEG = FL::NSEG, RPL = FL::RPL, RPW = FL::RPW;
+  constexpr int EPV = Elt<IT>::kPer16;
+  constexpr long kIo = sizeof(IT);
+  const int HV = a.v_heads, HK = a.k_heads, L = a.ring_len;
+  const int hk = hv / a.vpk;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 7;
+  const int row0 = wave * RPW + (lane >> 3);  // this lane's rows: row0 + 8*rr
+
+  char* const tptr = (char*)a.state + ((long)s * HV + hv) * (long)V * K * 4;
+  const rsrc_t trs = tile_rsrc(tptr, (uint32_t)(V * K * 4));
+  const uint32_t voff = (uint32_t)(row0 * K * 4 + m * 16);
+  const long kring0 = ((long)s * HK + hk) * (long)L * K;
+  const long vring0 = ((long)s * HV + hv) * (long)L * V;
+  const long gring0 = ((long)s * HV + hv) * L;
+  // the ring rows first (v rows to LDS, k rows into registers, gates by a
+  // clamped index: lanes at or past wn are never read), then the tile, so
+  // that waiting until only the tile's ITEMS loads are outstanding waits
+  // for exactly the ring rows (the k rows follow the DMA loop, so their own
+  // wait counts only the loads after them)
+  dma_rows(stage, (int)(SG::oV(L) / 16), wn * SG::VV, (const char*)a.v_ring + vring0 * kIo,
+           wave, lane, NT);
+  constexpr int KPT = (64 * K / EPV + NT - 1) / NT;  // k-ring vectors per thread, L <= 64
+  u32x4 kr[KPT];
+  const int nkv = wn * K / EPV;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = S[rr][sg * 4 + e] * gam;
-      st16_stream(tptr, (long)voff + rr * 8 * K * 4 + sg * 128, Elt<float>::pack(o));
-    }
+  for (int q = 0; q < KPT; ++q) {
+    const int e = tid + q * NT < nkv ? tid + q * NT : nkv - 1;  // clamped: no load in a branch
+    kr[q] = ld16(a.k_ring, (kring0 + (long)e * EPV) * kIo);
+  }
+  const int li = lane < wn ? lane : 0;
+  const float gl = a.g_ring[gring0 + li];
+  const float bl = a.beta_ring[gring0 + li];
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 sv[ITEMS];
+#pragma unroll
+  for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg)
+      sv[rr * NSEG + sg] = bload16_nt(trs, voff, rr * 8 * K * 4 + sg * 128);
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(ITEMS));  // the ring rows (older than the tile)
+  __builtin_amdgcn_sched_barrier(0);
+  // k rows 0..wn-1 to LDS as fp32
+  float* const K32 = reinterpret_cast<float*>(stage);
+  // (lanes past the last vector write that vector again: same values, no branch)
+#pragma unroll
+  for (int q = 0; q < KPT; ++q) {
+    const int e = tid + q * NT < nkv ? tid + q * NT : nkv - 1;
+    float f[EPV];
+    Elt<IT>::unpack(kr[q], f);
+#pragma unroll
+    for (int j = 0; j < EPV; j += 4)
+      *reinterpret_cast<u32x4*>(K32 + (long)e * EPV + j) = Elt<float>::pack(f + j);
+  }
+  lds_barrier();
+
+  float S[RPL][NSEG * 4];
+#pragma unroll
+  for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg) Elt<float>::unpack(sv[rr * NSEG + sg], &S[rr][sg * 4]);
+  fold_steps<IT, V, K, NT>(S, K32, stage + SG::oV(L),
+                           reinterpret_cast<float*>(stage + SG::oD(L)), gl, bl, wn, tid);
+#pragma unroll
+  for (int rr = 0; rr < RPL; ++rr)
+#pragma unroll
+    for (int sg = 0; sg < NSEG; ++sg)
+      st16_stream(tptr, (long)voff + rr * 8 * K * 4 + sg * 128, Elt<float>::pack(&S[rr][sg * 4]));
 }
 
 template <typename IT, int V, int K>
