@@ -206,11 +206,13 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
     dma_rows(lds, oK, w * QV, (const char*)a.k_ring + kring0 * kIo, wave, lane, NT);
     dma_rows(lds, oD, w * DV, (const char*)(a.d_ring + dring0), wave, lane, NT);
   }
-  // gate of ring entry `lane` (committed entries, then the drafts); 1 past them
-  float gl = 1.f;
-  if (lane < w) gl = a.g_ring[gring0 + lane];
-  else if (lane < w + T) gl = a.g[(long)(b * T + (lane - w)) * HV + hv];
-  const float bl = lane < T ? a.beta[(long)(b * T + lane) * HV + hv] : 0.f;
+  // gates: committed entries from the ring, the drafts from the inputs, both
+  // loaded by clamped indices (a load in a branch would make the compiler
+  // wait for every staged row before the tile is even issued); selected below
+  const int td = lane - w < 0 ? 0 : (lane - w < T ? lane - w : T - 1);
+  const float g_ring_l = a.g_ring[gring0 + (lane < w ? lane : 0)];
+  const float g_new_l = a.g[(long)(b * T + td) * HV + hv];
+  const float b_new_l = a.beta[(long)(b * T + (lane < T ? lane : T - 1)) * HV + hv];
   // the tile last: step 2 needs only the staged rows and the gates, so it
   // runs while the tile is still in flight (the scheduling barriers keep the
   // issue order the counter wait below relies on)
@@ -223,6 +225,9 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   __builtin_amdgcn_s_waitcnt((ITEMS & 15) | ((ITEMS >> 4) << 14));
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
+  // gate of ring entry `lane` (committed entries, then the drafts); 1 past them
+  const float gl = lane < w ? g_ring_l : (lane < w + T ? g_new_l : 1.f);
+  const float bl = lane < T ? b_new_l : 0.f;
 
   const char* Qs = lds;
   const char* Vs = lds + (long)oV * 16;
