@@ -353,7 +353,9 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps):
     """GDN speculative decoding from the ring: per round one verify of T drafts
     per row and one commit (accepted counts from a fixed seeded pattern; rows
     whose next verify would not fit fold their ring by the exact recurrence).
-    Algorithmic bytes are counted per launch from every row's cursor."""
+    Every timed region starts from empty rings, runs `rounds` untimed rounds
+    and then times the next `rounds` (the same rounds in every region);
+    algorithmic bytes are counted per launch from every row's cursor."""
     import linear_recurrence_amd as R
     HK, HV, K, V, L, nb = wl.k_heads, wl.v_heads, wl.dk, wl.dv, wl.ring_len, wl.batch
     ns = 2 * nb
@@ -411,20 +413,33 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps):
             bytes_total[0] += float(per_row.sum())
         d["w"] = np.where(fold, 0, wn)
 
+    def reset():
+        # every region starts from empty rings, so all regions run the same
+        # rounds (the same folds, the same bytes)
+        torch.cuda.synchronize()
+        for d in lay:
+            d["wp"].zero_()
+            d["nwp"].zero_()
+            d["w"][:] = 0
+
+    # per region: empty rings, `rounds` untimed rounds (every row's fold cycle
+    # is shorter), then `rounds` timed rounds, the same ones in every region
     for i in range(warmup):
         rnd(i, False)
     torch.cuda.synchronize()
     ts, bs = [], []
     for r in range(reps):
+        reset()
+        for i in range(rounds):
+            rnd(i, False)
         bytes_total[0] = 0.0
-        start = warmup + r * rounds
-        ts.append(time_region(lambda i: rnd(start + i), rounds, 0))
+        ts.append(time_region(lambda i: rnd(rounds + i), rounds, 0))
         bs.append(bytes_total[0])
-    for l in range(layers):
-        assert np.array_equal(lay[l]["wp"].cpu().numpy(), lay[l]["w"]), "spec cursor drift"
-    k = int(np.argsort(ts)[len(ts) // 2])
-    t = ts[k]
-    bytes_total[0] = bs[k]
+        for l in range(layers):
+            assert np.array_equal(lay[l]["wp"].cpu().numpy(), lay[l]["w"]), "spec cursor drift"
+    assert max(bs) == min(bs)
+    t = float(np.median(ts))
+    bytes_total[0] = bs[0]
     acc_mean = float(np.mean([a.mean() for a in accepts]))
     res = {
         "workload": f"gdn_spec_b{nb}_hk{HK}_hv{HV}_k{K}_L{L}_T{T}",
