@@ -25,10 +25,11 @@ def _unit(rng, shape):
 
 
 def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32, offset=0,
-             gates=None):
+             gates=None, force_p=0.1):
     """offset > 0 places the cursors and accepted counts `offset` int32s off
     a 16-byte boundary.  gates(rng, shape) draws the decays g (default:
-    exp(-softplus(N(0, 1)))))."""
+    exp(-softplus(N(0, 1)))).  force_p: the chance that a row's commit is
+    forced to fold."""
     print(f"case: spec nb={nb} HK={HK} HV={HV} K={K} V={V} L={L} T={T} io={io} "
           f"offset={offset}", flush=True)
     rng = np.random.default_rng(seed)
@@ -82,7 +83,7 @@ def run_spec(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32
             bound = np.maximum(1e-2, np.abs(o_ref) * 2**-7)
             assert (d <= bound).all(), f"round {r}: o error {d.max():.2e}"
         acc = rng.integers(0, T + 1, nb).astype(np.int32)
-        force = (rng.random(nb) < 0.1).astype(np.uint8)
+        force = (rng.random(nb) < force_p).astype(np.uint8)
         acc_t = acc_buf[offset:]
         acc_t.copy_(torch.tensor(acc, device=dev))
         R.replayssm_gdn_spec_commit(st, kr, gr, vr, br, sl, wp, acc_t,
@@ -149,6 +150,14 @@ def test_spec_fold_with_extreme_decays(io):
     L = 64 if io == torch.bfloat16 else 48
     run_spec(6, 2, 4, 128, 128, L, 8, io, 24, range(6), seed=95, gates=_extreme_gates)
     run_spec(6, 1, 2, 64, 128, 16, 4, io, 16, range(6), seed=96, gates=_extreme_gates)
+
+
+def test_spec_commit_every_row_folds():
+    """Every commit forced: all 256 x 32 (row, value head) tiles fold each
+    round, eight fold tasks per workgroup of the commit's 1024-workgroup
+    grid."""
+    run_spec(256, 16, 32, 128, 128, 16, 4, torch.bfloat16, 4, [0, 77, 200, 255], seed=97,
+             force_p=1.0)
 
 
 def test_spec_commit_large_batch_and_unaligned_cursors():
