@@ -143,7 +143,9 @@ __device__ static inline void dma_rows(char* lds, int c0, int n, const char* src
   }
 }
 
-template <typename IT, typename OT, int V, int K, bool MF>
+// TM: draft capacity of the per-draft tables and loops (4 when T <= 4, else
+// kMaxDraft), so a short draft chain does not pay for eight.
+template <typename IT, typename OT, int V, int K, bool MF, int TM>
 __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_kernel(const SpecArgs a) {
   using GS = GdnShape<V, K, true>;
   using SG = VerifyStage<IT, V, K>;
@@ -158,9 +160,9 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   // [i][t]: gamma_{i,t} (k_i . k_{w+t}) for i < w+t, gamma_{i,t} (k_i . q_t)
   // for i <= w+t; entry-major, so one entry's weights for all drafts are one
   // vector read
-  __shared__ __attribute__((aligned(16))) float cK[64][kMaxDraft];
-  __shared__ __attribute__((aligned(16))) float cQ[64][kMaxDraft];
-  __shared__ float gamS[kMaxDraft];    // Gamma_t = prod_{j <= w+t} g_j
+  __shared__ __attribute__((aligned(16))) float cK[64][TM];
+  __shared__ __attribute__((aligned(16))) float cQ[64][TM];
+  __shared__ float gamS[TM];    // Gamma_t = prod_{j <= w+t} g_j
 
   const int HV = a.v_heads, HK = a.k_heads, T = a.n_draft, L = a.ring_len;
   const int tile = xcd_tile(blockIdx.x, gridDim.x);
@@ -271,26 +273,26 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
 
   // ---- 4 (per state row, the drafts in order), given S0.k_{w+t}, S0.q_t
   auto draft_row = [&](int vr, const float* pkv, const float* pqv, bool writer) {
-    float hist_k[kMaxDraft], hist_q[kMaxDraft];  // committed-entry terms per draft
+    float hist_k[TM], hist_q[TM];  // committed-entry terms per draft
 #pragma unroll
-    for (int t = 0; t < kMaxDraft; ++t) hist_k[t] = hist_q[t] = 0.f;
+    for (int t = 0; t < TM; ++t) hist_k[t] = hist_q[t] = 0.f;
     for (int i = 0; i < w; ++i) {
       const float di = Ds[i * V + vr];
-      float ck[kMaxDraft], cq[kMaxDraft];
+      float ck[TM], cq[TM];
 #pragma unroll
-      for (int t = 0; t < kMaxDraft; ++t) {
+      for (int t = 0; t < TM; ++t) {
         ck[t] = cK[i][t];
         cq[t] = cQ[i][t];
       }
 #pragma unroll
-      for (int t = 0; t < kMaxDraft; ++t) {  // sums past T are never used
+      for (int t = 0; t < TM; ++t) {  // sums past T are never used
         hist_k[t] = fmaf(ck[t], di, hist_k[t]);
         hist_q[t] = fmaf(cq[t], di, hist_q[t]);
       }
     }
-    float dn[kMaxDraft];
+    float dn[TM];
 #pragma unroll
-    for (int t = 0; t < kMaxDraft; ++t) {
+    for (int t = 0; t < TM; ++t) {
       dn[t] = 0.f;
       if (t < T) {
         const float G = gamS[t];
@@ -365,9 +367,9 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
       const float* Pr = reinterpret_cast<const float*>(lds + (long)SG::chunks(T, L) * 16) +
                         ((vr & 7) >> 1) * VerifyMfma::kRegionFloats +
                         (2 * (vr >> 3) + (vr & 1)) * 16;
-      float pkv[kMaxDraft], pqv[kMaxDraft];
+      float pkv[TM], pqv[TM];
 #pragma unroll
-      for (int t = 0; t < kMaxDraft; ++t) {
+      for (int t = 0; t < TM; ++t) {
         pkv[t] = t < T ? Pr[t] : 0.f;
         pqv[t] = t < T ? Pr[T + t] : 0.f;
       }
@@ -377,9 +379,9 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
     // ---- 3. S0 . k_{w+t} and S0 . q_t for this lane's state rows
     const int c = tid % LPR;
     const int prow = tid / LPR;
-    float pk[kMaxDraft][RR::NF], pq[kMaxDraft][RR::NF];
+    float pk[TM][RR::NF], pq[TM][RR::NF];
 #pragma unroll
-    for (int t = 0; t < kMaxDraft; ++t) {
+    for (int t = 0; t < TM; ++t) {
       if (t < T) {
         float kseg[SV], qseg[SV];
         LdsRead<IT>::template seg<SV>(Ks + (long)(w + t) * QV * 16, c * SV, kseg);
@@ -410,9 +412,9 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
     const bool writer = (c % RR::DUP) == 0;
 #pragma unroll
     for (int j = 0; j < RR::NF; ++j) {
-      float pkv[kMaxDraft], pqv[kMaxDraft];
+      float pkv[TM], pqv[TM];
 #pragma unroll
-      for (int t = 0; t < kMaxDraft; ++t) {
+      for (int t = 0; t < TM; ++t) {
         pkv[t] = t < T ? pk[t][j] : 0.f;
         pqv[t] = t < T ? pq[t][j] : 0.f;
       }
@@ -784,22 +786,29 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_ke
 // bf16 inputs at V = K = 128 take the matrix-core products when the extra
 // LDS fits; otherwise (fp32 inputs, other shapes, the largest rings) the
 // vector path.
-template <typename IT, typename OT, int V, int K>
-static int launch_verify(const SpecArgs& a, int batch, hipStream_t stream) {
+template <typename IT, typename OT, int V, int K, int TM>
+static int launch_verify_tm(const SpecArgs& a, int batch, hipStream_t stream) {
   using SG = VerifyStage<IT, V, K>;
   constexpr int NT = GdnShape<V, K, true>::NT;
-  const size_t fixed = (2 * kMaxDraft * 64 + kMaxDraft) * sizeof(float);
+  const size_t fixed = (2 * TM * 64 + TM) * sizeof(float);
   const unsigned grid = (unsigned)((long)batch * a.v_heads);
   const size_t lds = (size_t)SG::chunks(a.n_draft, a.ring_len) * 16;
   if constexpr (std::is_same<IT, bf16>::value && V == 128 && K == 128 && NT == 256) {
     if (lds + VerifyMfma::kBytes + fixed <= kMaxLds)
       return launch_kernel(
-          reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, true>), grid, NT,
-          lds + VerifyMfma::kBytes, stream, a);
+          reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, true, TM>), grid,
+          NT, lds + VerifyMfma::kBytes, stream, a);
   }
   if (lds + fixed > kMaxLds) return RSSM_ESHAPE;  // staged rows must fit one workgroup's LDS
-  return launch_kernel(reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, false>),
-                       grid, NT, lds, stream, a);
+  return launch_kernel(
+      reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, false, TM>), grid, NT,
+      lds, stream, a);
+}
+
+template <typename IT, typename OT, int V, int K>
+static int launch_verify(const SpecArgs& a, int batch, hipStream_t stream) {
+  return a.n_draft <= 4 ? launch_verify_tm<IT, OT, V, K, 4>(a, batch, stream)
+                        : launch_verify_tm<IT, OT, V, K, kMaxDraft>(a, batch, stream);
 }
 
 // Grid of the task-list commit: enough resident workgroups to keep every CU
