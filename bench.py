@@ -703,6 +703,8 @@ def main():
               "standard_updates_per_s": t["standard"]["state_updates_per_s"],
               "standard_GBps": t["standard"]["achieved_GBps"],
               "standard_us_per_launch": t["standard"]["ms_per_step"] * 1e3,
+              "replay_region_us_per_launch": t["replay"]["region_us_per_launch"],
+              "standard_region_us_per_launch": t["standard"]["region_us_per_launch"],
               "speedup": t["replay"]["state_updates_per_s"]
               / t["standard"]["state_updates_per_s"],
               "spread": [t["replay"]["spread"], t["standard"]["spread"]]}
