@@ -269,7 +269,10 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
       cQ[lane][t] = lane <= p ? gam * kq : 0.f;
     }
   }
-  __syncthreads();
+  // (no barrier here: only the draft walk reads cK, cQ and gamS; step 3
+  // reads the staged rows and the tile and writes per-wave LDS regions, so
+  // each wave starts it as soon as its own tile has landed, and the barrier
+  // before the walk covers both steps)
 
   // ---- 4 (per state row, the drafts in order), given S0.k_{w+t}, S0.q_t
   auto draft_row = [&](int vr, const float* pkv, const float* pqv, bool writer) {
@@ -410,6 +413,7 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
       }
     }
     const bool writer = (c % RR::DUP) == 0;
+    __syncthreads();  // the weighted dots of step 2 are in LDS
 #pragma unroll
     for (int j = 0; j < RR::NF; ++j) {
       float pkv[TM], pqv[TM];
