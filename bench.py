@@ -694,8 +694,10 @@ def main():
         # 16 rotated layers so the working set stays far above the last-level cache
         wl_tp = dataclasses.replace(wl, name="mamba2_b512_h10_L16_bf16state_tp8share",
                                     nheads=10)
-        t = bench_mamba2(wl_tp, args.tp_layers, args.steps, args.warmup, y_dtype, dev, reps,
-                         ordered=False)
+        # warm-up: at least four passes over the rotated layers (a pass is
+        # 128 launches here, ~3 ms)
+        t = bench_mamba2(wl_tp, args.tp_layers, args.steps, max(args.warmup, 4 * args.tp_layers),
+                         y_dtype, dev, reps, ordered=False)
         tp = {"workload": wl_tp.name, "nheads": 10, "layers_rotated": args.tp_layers,
               "replay_updates_per_s": t["replay"]["state_updates_per_s"],
               "replay_GBps": t["replay"]["achieved_GBps"], "replay_frac": t["replay"]["frac"],
