@@ -23,7 +23,9 @@ order; same results, bit for bit); the standard read+write update
 rounding of the bf16 write-back; one tensor-parallel rank's share of the
 layer (10 of 80 heads); the GDN replay/standard decode at batch 256 (16 key
 / 32 value heads, K = V = 128, L = 16, bf16 q/k/v, fp32 state) and its
-speculative verify + commit with 4 drafts per round; the KDA
+speculative verify + commit with 4 drafts per round (and the deferred-fold
+rounds: a verify that folds the rows marked by the previous round, then the
+cursor advance); the KDA
 (per-key-channel gate) replay/standard decode at batch 256, 32 heads,
 K = V = 128, L = 16; the host metadata builder; and the float64 CPU oracle
 on a bounded sample, both the ReplaySSM reconstruction and the standard
@@ -349,10 +351,13 @@ def bench_gdn(wl, layers, steps, warmup, dev, reps):
     return res
 
 
-def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps):
+def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps, deferred=False):
     """GDN speculative decoding from the ring: per round one verify of T drafts
     per row and one commit (accepted counts from a fixed seeded pattern; rows
     whose next verify would not fit fold their ring by the exact recurrence).
+    deferred: the deferred-fold rounds instead, a verify that first folds the
+    rows marked by the previous round, then the cursor advance (the fold then
+    reuses the verify's read of the state tile).
     Every timed region starts from empty rings, runs `rounds` untimed rounds
     and then times the next `rounds` (the same rounds in every region);
     algorithmic bytes are counted per launch from every row's cursor."""
@@ -373,7 +378,10 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps):
                         vr=torch.zeros((ns, HV, L, V), dtype=io, device=dev),
                         br=torch.zeros((ns, HV, L), device=dev),
                         wp=torch.zeros(nb, dtype=torch.int32, device=dev),
-                        nwp=torch.zeros(nb, dtype=torch.int32, device=dev), w=np.zeros(nb, np.int64)))
+                        nwp=torch.zeros(nb, dtype=torch.int32, device=dev),
+                        fl=torch.zeros(nb, dtype=torch.uint8, device=dev),
+                        nfl=torch.zeros(nb, dtype=torch.uint8, device=dev),
+                        w=np.zeros(nb, np.int64), f=np.zeros(nb, bool)))
     slots = torch.tensor(rng.permutation(ns)[:nb].astype(np.int32), device=dev)
 
     def unit(shape):
@@ -397,21 +405,40 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps):
     def rnd(i, count=True):
         d = lay[i % layers]
         inp_i = inputs[i % 4]
-        R.replayssm_gdn_spec_verify(d["st"], d["dr"], d["kr"], d["gr"], d["vr"], d["br"], slots,
-                                    d["wp"], inp_i["q"], inp_i["k"], inp_i["v"], inp_i["g"],
-                                    inp_i["beta"], o=o)
         a = accepts[i % 8]
-        R.replayssm_gdn_spec_commit(d["st"], d["kr"], d["gr"], d["vr"], d["br"], slots, d["wp"],
-                                    acc_t[i % 8], T, d["nwp"])
-        d["wp"], d["nwp"] = d["nwp"], d["wp"]
         w = d["w"]
-        wn = w + a
-        fold = wn + T > L
-        if count:
-            per_row = (tile + w * entry + T * (entry + V * sio + 4) + inp + 4) * HV \
-                + np.where(fold, (2 * tile + wn * raw) * HV, 0) + 12
-            bytes_total[0] += float(per_row.sum())
-        d["w"] = np.where(fold, 0, wn)
+        if deferred:
+            R.replayssm_gdn_spec_verify_flush(d["st"], d["dr"], d["kr"], d["gr"], d["vr"],
+                                              d["br"], slots, d["wp"], d["fl"], inp_i["q"],
+                                              inp_i["k"], inp_i["v"], inp_i["g"], inp_i["beta"],
+                                              o=o)
+            R.replayssm_gdn_spec_advance(d["kr"], slots, d["wp"], d["fl"], acc_t[i % 8], T,
+                                         inp_i["k"], d["nwp"], d["nfl"])
+            d["fl"], d["nfl"] = d["nfl"], d["fl"]
+            f = d["f"]
+            wv = np.where(f, 0, w)
+            if count:
+                # a folding row: the tile write and its raw rows (the tile
+                # read is the verify's); the advance re-reads its drafts' k
+                per_row = (tile + wv * entry + T * (entry + V * sio + 4) + inp + 4) * HV \
+                    + np.where(f, (tile + w * raw) * HV + T * HK * K * sio, 0) + 18
+                bytes_total[0] += float(per_row.sum())
+            d["w"] = wv + a
+            d["f"] = d["w"] + T > L
+        else:
+            R.replayssm_gdn_spec_verify(d["st"], d["dr"], d["kr"], d["gr"], d["vr"], d["br"],
+                                        slots, d["wp"], inp_i["q"], inp_i["k"], inp_i["v"],
+                                        inp_i["g"], inp_i["beta"], o=o)
+            R.replayssm_gdn_spec_commit(d["st"], d["kr"], d["gr"], d["vr"], d["br"], slots,
+                                        d["wp"], acc_t[i % 8], T, d["nwp"])
+            wn = w + a
+            fold = wn + T > L
+            if count:
+                per_row = (tile + w * entry + T * (entry + V * sio + 4) + inp + 4) * HV \
+                    + np.where(fold, (2 * tile + wn * raw) * HV, 0) + 12
+                bytes_total[0] += float(per_row.sum())
+            d["w"] = np.where(fold, 0, wn)
+        d["wp"], d["nwp"] = d["nwp"], d["wp"]
 
     def reset():
         # every region starts from empty rings, so all regions run the same
@@ -420,7 +447,10 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps):
         for d in lay:
             d["wp"].zero_()
             d["nwp"].zero_()
+            d["fl"].zero_()
+            d["nfl"].zero_()
             d["w"][:] = 0
+            d["f"][:] = False
 
     # per region: empty rings, `rounds` untimed rounds (every row's fold cycle
     # is shorter), then `rounds` timed rounds, the same ones in every region
@@ -442,7 +472,7 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps):
     bytes_total[0] = bs[0]
     acc_mean = float(np.mean([a.mean() for a in accepts]))
     res = {
-        "workload": f"gdn_spec_b{nb}_hk{HK}_hv{HV}_k{K}_L{L}_T{T}",
+        "workload": f"gdn_spec{'_deferred' if deferred else ''}_b{nb}_hk{HK}_hv{HV}_k{K}_L{L}_T{T}",
         "drafts_per_round": T, "mean_accepted": acc_mean,
         "rounds_per_s": rounds / t, "us_per_round": t / rounds * 1e6,
         "verified_tokens_per_s": nb * T * rounds / t,
@@ -736,10 +766,13 @@ def main():
         kda = bench_gdn(KDA, args.layers, args.steps, args.warmup, dev, reps)
         print(f"[bench] kda done: {kda['replay_GBps']:.0f} GB/s replay", file=sys.stderr,
               flush=True)
-    spec = None
+    spec = spec_def = None
     if not args.no_gdn:
         spec = bench_gdn_spec(GDN, 4, args.layers, 256, 16, dev, reps)
         print(f"[bench] gdn spec done: {spec['GBps']:.0f} GB/s", file=sys.stderr, flush=True)
+        spec_def = bench_gdn_spec(GDN, 4, args.layers, 256, 16, dev, reps, deferred=True)
+        print(f"[bench] gdn spec (deferred folds) done: {spec_def['us_per_round']:.1f} us/round",
+              file=sys.stderr, flush=True)
 
     traffic, traffic_note = measured_traffic(args.traffic_json)
     line = {
@@ -785,6 +818,7 @@ def main():
         "gdn": gdn,
         "kda": kda,
         "gdn_spec": spec,
+        "gdn_spec_deferred": spec_def,
         "stochastic_rounding": (None if "sr_replay" not in m else {
             "replay_updates_per_s": m["sr_replay"]["state_updates_per_s"],
             "replay_GBps": m["sr_replay"]["achieved_GBps"],

@@ -365,6 +365,56 @@ int replayssm_gdn_spec_commit(const rssm_gdn_dims* dims, int32_t n_draft, void* 
                               int32_t* status, hipStream_t stream);
 
 /*
+ * Deferred-fold rounds (the same method with the fold moved into the next
+ * verify, where it reuses that verify's read of the state tile: sglang
+ * #28695 Implementation items 2-4 name a per-slot is_flush cursor next to
+ * write_pos, and the exact fold runs on flush).  A round is
+ * replayssm_gdn_spec_verify_flush then replayssm_gdn_spec_advance; between
+ * rounds a row's logical state is its checkpoint folded with ring entries
+ * 0..write_pos-1, and is_flush marks rows whose next verify folds first.
+ * Cursors start at write_pos = 0, is_flush = 0.  A row keeps to one kind of
+ * round (a pending fold is not visible to replayssm_gdn_spec_verify).
+ *
+ * replayssm_gdn_spec_verify_flush - rows with is_flush[b] != 0 (is_flush
+ * [batch] uint8, required) first fold ring entries 0..write_pos[b]-1 into
+ * the state exactly as replayssm_gdn_spec_commit does (0 <= write_pos[b] <=
+ * L, else RSSM_ST_RING_OVERFLOW), store it, then verify their drafts at ring
+ * entries 0..T-1; their drafts' k rows are left to
+ * replayssm_gdn_spec_advance (the other value heads of the key head may
+ * still be reading the old ones).  Other rows: as replayssm_gdn_spec_verify.
+ * Arguments otherwise as replayssm_gdn_spec_verify, with the state written.
+ * A folding row stages the k and v rows of the whole ring next to the
+ * verify's own rows: RSSM_ESHAPE when they do not fit one workgroup's 64 KB
+ * of LDS (at K = V = 128 the longest rings are 46 entries for T <= 4 and 42
+ * for T = 8 with bf16 inputs, 27 and 24 with fp32 ones).
+ *
+ * replayssm_gdn_spec_advance - after the verify, with accepted[b] (0..T)
+ * drafts kept: w = is_flush[b] ? 0 : write_pos[b]; w' = w + accepted[b];
+ * next_write_pos[b] = w'; next_is_flush[b] = (w' + T > L) or
+ * force_flush[b] (may be NULL).  Rows with is_flush[b] set also receive the
+ * k rows of their T drafts (k [batch, T, HK, K] io_dtype [16B], this round's
+ * verify input) at k_ring entries 0..T-1 of their key heads.  The next_*
+ * buffers must not alias write_pos / is_flush.  dims as for the verify (only
+ * batch, k_heads, dk, ring_len, num_slots and io_dtype are used).  accepted outside [0, T] sets RSSM_ST_RING_OVERFLOW and is clamped; a slot
+ * out of range sets RSSM_ST_BAD_SLOT and its row is not marked.
+ */
+int replayssm_gdn_spec_verify_flush(const rssm_gdn_dims* dims, int32_t n_draft,
+                                    float* state, float* d_ring, void* k_ring,
+                                    float* g_ring, void* v_ring, float* beta_ring,
+                                    const int32_t* slot_idx, const int32_t* write_pos,
+                                    const uint8_t* is_flush, const void* q,
+                                    const void* k, const void* v, const float* g,
+                                    const float* beta, void* o, int32_t* status,
+                                    hipStream_t stream);
+
+int replayssm_gdn_spec_advance(const rssm_gdn_dims* dims, int32_t n_draft, void* k_ring,
+                               const void* k, const int32_t* slot_idx,
+                               const int32_t* write_pos, const uint8_t* is_flush,
+                               const int32_t* accepted, const uint8_t* force_flush,
+                               int32_t* next_write_pos, uint8_t* next_is_flush,
+                               int32_t* status, hipStream_t stream);
+
+/*
  * Host-side metadata (HOST pointers; plain CPU code, nothing is enqueued).
  *
  * replayssm_build_metadata - per-row cursors of one decode step from token

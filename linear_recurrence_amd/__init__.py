@@ -20,8 +20,8 @@ import torch  # loads the HIP runtime the library then binds to
 __all__ = [
     "ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
     "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
-    "replayssm_gdn_spec_commit", "kda_standard_decode", "replayssm_kda_decode",
-    "build_metadata", "flush_first_order",
+    "replayssm_gdn_spec_commit", "replayssm_gdn_spec_verify_flush", "replayssm_gdn_spec_advance",
+    "kda_standard_decode", "replayssm_kda_decode", "build_metadata", "flush_first_order",
     "check_copy_sources", "library_path", "load",
     "RssmError", "ST_BAD_WRITE_POS", "ST_RING_OVERFLOW", "ST_BAD_SLOT",
     "ST_BAD_ROW", "EXPORTS",
@@ -33,7 +33,8 @@ F32, BF16 = 0, 1
 ST_BAD_WRITE_POS, ST_RING_OVERFLOW, ST_BAD_SLOT, ST_BAD_ROW = 1, 2, 4, 8
 EXPORTS = ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
            "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
-           "replayssm_gdn_spec_commit", "kda_standard_decode", "replayssm_kda_decode",
+           "replayssm_gdn_spec_commit", "replayssm_gdn_spec_verify_flush",
+           "replayssm_gdn_spec_advance", "kda_standard_decode", "replayssm_kda_decode",
            "replayssm_build_metadata", "replayssm_decode_ordered", "replayssm_flush_first_order",
            "replayssm_check_copy_sources", "replayssm_strerror", "replayssm_abi_version")
 
@@ -92,11 +93,14 @@ def load():
     lib.replayssm_gdn_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 17
     lib.replayssm_gdn_spec_verify.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 16
     lib.replayssm_gdn_spec_commit.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 13
+    lib.replayssm_gdn_spec_verify_flush.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 17
+    lib.replayssm_gdn_spec_advance.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 11
     lib.kda_standard_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 10
     lib.replayssm_kda_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 17
     for fn in ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
                "gdn_standard_decode", "replayssm_gdn_decode", "replayssm_gdn_spec_verify",
-               "replayssm_gdn_spec_commit", "kda_standard_decode", "replayssm_kda_decode"):
+               "replayssm_gdn_spec_commit", "replayssm_gdn_spec_verify_flush",
+               "replayssm_gdn_spec_advance", "kda_standard_decode", "replayssm_kda_decode"):
         getattr(lib, fn).restype = ctypes.c_int
     lib.replayssm_build_metadata.argtypes = [I, I, I, P, P, P, P, P]
     lib.replayssm_build_metadata.restype = ctypes.c_int
@@ -458,6 +462,26 @@ def replayssm_gdn_spec_verify(state, d_ring, k_ring, g_ring, v_ring, beta_ring, 
     [batch, T, HV] float32; o [batch, T, HV, V].  Writes ring entries
     w..w+T-1; leaves the state and the cursors alone.
     """
+    return _spec_verify("replayssm_gdn_spec_verify", state, d_ring, k_ring, g_ring, v_ring,
+                        beta_ring, slot_idx, write_pos, None, q, k, v, g, beta, o, scale, status,
+                        out_dtype, stream)
+
+
+def replayssm_gdn_spec_verify_flush(state, d_ring, k_ring, g_ring, v_ring, beta_ring, slot_idx,
+                                    write_pos, is_flush, q, k, v, g, beta, o=None, scale=None,
+                                    status=None, out_dtype=None, stream=None):
+    """The verify of the deferred-fold rounds: rows with is_flush [batch]
+    (uint8) set first fold ring entries 0..w-1 into the state by the exact
+    recurrence, then verify their drafts at entries 0..T-1 (their k rows are
+    written by replayssm_gdn_spec_advance); the other rows as in
+    replayssm_gdn_spec_verify.  Returns o."""
+    return _spec_verify("replayssm_gdn_spec_verify_flush", state, d_ring, k_ring, g_ring,
+                        v_ring, beta_ring, slot_idx, write_pos, is_flush, q, k, v, g, beta, o,
+                        scale, status, out_dtype, stream)
+
+
+def _spec_verify(fn, state, d_ring, k_ring, g_ring, v_ring, beta_ring, slot_idx, write_pos,
+                 is_flush, q, k, v, g, beta, o, scale, status, out_dtype, stream):
     dev = _need(state, "state", torch.float32).device
     ns, HV, V, K = state.shape
     _need(q, "q", (torch.float32, torch.bfloat16), dev=dev)
@@ -471,17 +495,21 @@ def replayssm_gdn_spec_verify(state, d_ring, k_ring, g_ring, v_ring, beta_ring, 
     _, L = _spec_rings(state, d_ring, k_ring, g_ring, v_ring, beta_ring, io, dev)
     _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
     _need(write_pos, "write_pos", torch.int32, (nb,), dev=dev)
+    if is_flush is not None:
+        _need(is_flush, "is_flush", torch.uint8, (nb,), dev=dev)
     _opt(status, "status", torch.int32, (1,))
     if o is None:
         o = torch.empty((nb, T, HV, V), dtype=out_dtype or io, device=dev)
     _need(o, "o", (torch.float32, torch.bfloat16), (nb, T, HV, V), dev=dev)
     d = GdnDims(nb, HK, HV, K, V, L, ns, F32, _DT[io], _DT[o.dtype],
                 0.0 if scale is None else float(scale))
-    rc = load().replayssm_gdn_spec_verify(
-        ctypes.byref(d), ctypes.c_int32(T), _ptr(state), _ptr(d_ring), _ptr(k_ring),
-        _ptr(g_ring), _ptr(v_ring), _ptr(beta_ring), _ptr(slot_idx), _ptr(write_pos), _ptr(q),
-        _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o), _ptr(status), _stream(stream))
-    _check("replayssm_gdn_spec_verify", rc)
+    head = [ctypes.byref(d), ctypes.c_int32(T), _ptr(state), _ptr(d_ring), _ptr(k_ring),
+            _ptr(g_ring), _ptr(v_ring), _ptr(beta_ring), _ptr(slot_idx), _ptr(write_pos)]
+    if is_flush is not None:
+        head.append(_ptr(is_flush))
+    rc = getattr(load(), fn)(*head, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o),
+                             _ptr(status), _stream(stream))
+    _check(fn, rc)
     return o
 
 
@@ -508,3 +536,33 @@ def replayssm_gdn_spec_commit(state, k_ring, g_ring, v_ring, beta_ring, slot_idx
         _ptr(v_ring), _ptr(beta_ring), _ptr(slot_idx), _ptr(write_pos), _ptr(accepted),
         _ptr(force_flush), _ptr(next_write_pos), _ptr(flushed), _ptr(status), _stream(stream))
     _check("replayssm_gdn_spec_commit", rc)
+
+
+def replayssm_gdn_spec_advance(k_ring, slot_idx, write_pos, is_flush, accepted, n_draft, k,
+                               next_write_pos, next_is_flush, force_flush=None, status=None,
+                               stream=None):
+    """Cursor advance of the deferred-fold rounds (no fold here): a row that
+    folded in this round's verify (is_flush set) restarts from entry 0 and
+    receives its drafts' k rows (k [batch, T, HK, K], this round's input) at
+    ring entries 0..T-1; then w' = w + accepted and next_is_flush = (w' + T >
+    L) or force_flush."""
+    dev = k_ring.device
+    io = k_ring.dtype
+    _need(k_ring, "k_ring", (torch.float32, torch.bfloat16), dev=dev)
+    ns, HK, L, K = k_ring.shape
+    nb = slot_idx.shape[0]
+    _need(k, "k", io, (nb, n_draft, HK, K), dev=dev)
+    _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
+    _need(write_pos, "write_pos", torch.int32, (nb,), dev=dev)
+    _need(is_flush, "is_flush", torch.uint8, (nb,), dev=dev)
+    _need(accepted, "accepted", torch.int32, (nb,), dev=dev)
+    _need(next_write_pos, "next_write_pos", torch.int32, (nb,), dev=dev)
+    _need(next_is_flush, "next_is_flush", torch.uint8, (nb,), dev=dev)
+    _opt(force_flush, "force_flush", torch.uint8, (nb,), dev=dev)
+    _opt(status, "status", torch.int32, (1,))
+    d = GdnDims(nb, HK, HK, K, K, L, ns, F32, _DT[io], _DT[io], 0.0)  # value heads unused
+    rc = load().replayssm_gdn_spec_advance(
+        ctypes.byref(d), ctypes.c_int32(n_draft), _ptr(k_ring), _ptr(k), _ptr(slot_idx),
+        _ptr(write_pos), _ptr(is_flush), _ptr(accepted), _ptr(force_flush),
+        _ptr(next_write_pos), _ptr(next_is_flush), _ptr(status), _stream(stream))
+    _check("replayssm_gdn_spec_advance", rc)

@@ -79,7 +79,9 @@ struct SpecArgs {
   int32_t n_draft;
   float scale;
   int32_t fold_tasks;  // commit: a small grid working through a list of fold tasks
-  int32_t n_rows;      // commit: batch rows
+  int32_t n_rows;      // commit, advance: batch rows
+  const uint8_t* is_flush;  // verify with flush, advance: rows whose ring folds before the verify
+  uint8_t* next_is_flush;   // advance: the next round's flags
 };
 
 // Commit decision of one row: the cursor after its accepted drafts (clamped
@@ -133,6 +135,19 @@ struct VerifyMfma {
   static constexpr size_t kBytes = 4 * kRegionFloats * sizeof(float);
 };
 
+// Dynamic LDS of the verify: the staged rows, then the matrix-core regions.
+template <typename IT, int V, int K, bool MF>
+__host__ __device__ constexpr size_t verify_lds_bytes(int T, int L) {
+  return (size_t)VerifyStage<IT, V, K>::chunks(T, L) * 16 + (MF ? VerifyMfma::kBytes : 0);
+}
+
+// A folding row's stage after it: k rows and v rows of the whole ring as
+// stored, then two V-float buffers of d.
+template <typename IT, int V, int K>
+constexpr size_t verify_fold_bytes(int L) {
+  return (size_t)L * (K + V) * sizeof(IT) + 2 * V * sizeof(float);
+}
+
 // 16-byte chunks [c0, c0+n) of LDS from global memory, one wave-wide
 // direct-to-LDS load per 64 chunks; chunk u comes from src + 16*u.
 __device__ static inline void dma_rows(char* lds, int c0, int n, const char* src, int wave,
@@ -143,9 +158,133 @@ __device__ static inline void dma_rows(char* lds, int c0, int n, const char* src
   }
 }
 
+// The fold holds the tile as gam * S: a step's decay g multiplies the scalar
+// gam instead of every element, the row dot is gam * (S.k) and the rank-1
+// update adds (d / gam) k to S.  Algebraically the recurrence; when gam
+// would leave [2^-60, 2^60] (or g is 0 or not finite) the pending decay and
+// the step's own are applied to S element by element and gam restarts at 1.
+constexpr float kLazyFloor = 0x1p-60f, kLazyCeil = 0x1p60f;
+
+// Sums of ITEMS per-lane partials over the LPR (16 or 32) lanes of a state
+// row, folded as RowReduce does it (lane keeps the total of partial
+// RowReduce::item(0, lane)), by VALU lane exchanges only: lanes 16 apart by
+// a row swap (the two values each pair of lanes adds arrive in the two
+// swapped registers), then half-row mirror partners and quad permutations.
+template <int ITEMS, int LPR>
+struct FoldReduce {
+  static_assert(ITEMS == 16 && (LPR == 16 || LPR == 32), "fold reduce shape");
+  template <int ctrl>
+  __device__ static inline float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xF, 0xF, false));
+  }
+  template <int H, int O, int ctrl>
+  __device__ static inline void level(float (&v)[ITEMS], int lane) {
+    const bool up = (lane & O) != 0;
+#pragma unroll
+    for (int j = 0; j < H; ++j) {
+      const float send = up ? v[j] : v[j + H];
+      const float keep = up ? v[j + H] : v[j];
+      v[j] = keep + dpp<ctrl>(send);
+    }
+  }
+  __device__ static inline void run(float (&v)[ITEMS], int lane) {
+    if constexpr (LPR == 32) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]),
+                                                        __float_as_uint(v[j + 8]), false, false);
+        v[j] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      }
+      level<4, 8, 0x140>(v, lane);  // row mirror
+      level<2, 4, 0x141>(v, lane);  // half-row mirror
+      level<1, 2, 0x4E>(v, lane);   // quad xor 2
+      v[0] += dpp<0xB1>(v[0]);      // quad xor 1: two lanes hold each total
+    } else {
+      level<8, 8, 0x140>(v, lane);
+      level<4, 4, 0x141>(v, lane);
+      level<2, 2, 0x4E>(v, lane);
+      level<1, 1, 0xB1>(v, lane);
+    }
+  }
+};
+
+// The exact fold on the verify's tile layout (lane tid holds 16 bytes of
+// every NT*16-byte item: state row it*RPI + tid/LPR, columns SV*(tid%LPR)
+// onwards), for a row whose ring folds before its drafts are verified: the
+// same recurrence, lazy decay and order as the commit's fold, entries
+// 0..wn-1 from their raw inputs (k and v rows as stored in Ks, Vs; g and
+// beta of entry i in lane i of gl, bl); the row dots are folded sums over
+// the LPR lanes of a row (a row's lanes never span two waves) and each
+// row's d goes to its lanes through dbuf.
+template <typename IT, int V, int K, int ITEMS>
+__device__ static inline void fold_steps_v(u32x4 (&sv)[ITEMS], const char* Ks, const char* Vs,
+                                           float* dbuf, float gl, float bl, int wn, int tid) {
+  using GS = GdnShape<V, K, true>;
+  constexpr int SV = GS::SV, LPR = GS::LPR, RPI = GS::RPI;
+  static_assert(ITEMS == GS::ITEMS, "verify tile layout");
+  constexpr int QV = K / Elt<IT>::kPer16;
+  constexpr long kIo = sizeof(IT);
+  using RR = RowReduce<ITEMS, LPR>;
+  static_assert(RR::NF == 1 && ITEMS % 4 == 0, "one row total per lane");
+  const int c = tid % LPR;
+  const int prow = tid / LPR;
+  const int my_item = RR::item(0, tid);
+  const bool writer = (c % RR::DUP) == 0;
+  float S[ITEMS][SV];
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) Elt<float>::unpack(sv[it], S[it]);
+  float gam = 1.f;
+  for (int i = 0; i < wn; ++i) {
+    const float gi = lane_value(gl, i), bi = lane_value(bl, i);
+    float gn = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gam * gi)));
+    if (!(gn >= kLazyFloor && gn <= kLazyCeil)) {
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it)
+#pragma unroll
+        for (int e = 0; e < SV; ++e) S[it][e] = (S[it][e] * gam) * gi;
+      gn = 1.f;
+    }
+    float kv[SV];
+    LdsRead<IT>::template seg<SV>(Ks + (long)i * QV * 16, c * SV, kv);
+    float part[ITEMS];
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      float x = 0.f;
+#pragma unroll
+      for (int e = 0; e < SV; ++e) x = fmaf(S[it][e], kv[e], x);
+      part[it] = x;
+    }
+    FoldReduce<ITEMS, LPR>::run(part, tid);
+    const float rinv = 1.f / gn;
+    float* db = dbuf + (i & 1) * V;  // row it*RPI + prow at prow*ITEMS + it
+    if (writer) {
+      const float vr = LdsRead<IT>::one(Vs + (long)i * V * kIo, my_item * RPI + prow);
+      db[prow * ITEMS + my_item] = (bi * fmaf(-gn, part[0], vr)) * rinv;
+    }
+    __builtin_amdgcn_wave_barrier();  // a row's d comes from its own wave's lanes
+    float dv[ITEMS];
+#pragma unroll
+    for (int j = 0; j < ITEMS; j += 4)
+      Elt<float>::unpack(*reinterpret_cast<const u32x4*>(db + prow * ITEMS + j), dv + j);
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it)
+#pragma unroll
+      for (int e = 0; e < SV; ++e) S[it][e] = fmaf(dv[it], kv[e], S[it][e]);
+    gam = gn;
+  }
+#pragma unroll
+  for (int it = 0; it < ITEMS; ++it) {
+#pragma unroll
+    for (int e = 0; e < SV; ++e) S[it][e] *= gam;
+    sv[it] = Elt<float>::pack(S[it]);
+  }
+}
+
 // TM: draft capacity of the per-draft tables and loops (4 when T <= 4, else
-// kMaxDraft), so a short draft chain does not pay for eight.
-template <typename IT, typename OT, int V, int K, bool MF, int TM>
+// kMaxDraft), so a short draft chain does not pay for eight.  FL: rows with
+// is_flush set first fold ring entries 0..w-1 into the state (the exact fold
+// of the commit) and then verify their drafts at entries 0..T-1.
+template <typename IT, typename OT, int V, int K, bool MF, int TM, bool FL>
 __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_kernel(const SpecArgs a) {
   using GS = GdnShape<V, K, true>;
   using SG = VerifyStage<IT, V, K>;
@@ -174,10 +313,13 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   const int s = a.slot_idx[b];
-  const int w = a.write_pos[b];
+  const int w_in = a.write_pos[b];
+  const bool fold = FL && a.is_flush[b] != 0;
   int st = 0;
   if (s < 0 || s >= a.num_slots) st |= RSSM_ST_BAD_SLOT;
-  if (w < 0 || w + T > L) st |= RSSM_ST_RING_OVERFLOW;
+  if (w_in < 0 || (fold ? w_in > L : w_in + T > L)) st |= RSSM_ST_RING_OVERFLOW;
+  const int w = fold ? 0 : w_in;    // committed entries the drafts are verified against
+  const int wf = fold ? w_in : 0;   // entries folded into the state first
   if (st) {
     if (hv == 0 && tid == 0 && a.status) atomicOr(a.status, st);
     for (int e = tid; e < T * V; e += NT) {
@@ -208,11 +350,21 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
     dma_rows(lds, oK, w * QV, (const char*)a.k_ring + kring0 * kIo, wave, lane, NT);
     dma_rows(lds, oD, w * DV, (const char*)(a.d_ring + dring0), wave, lane, NT);
   }
-  // gates: committed entries from the ring, the drafts from the inputs, both
-  // loaded by clamped indices (a load in a branch would make the compiler
-  // wait for every staged row before the tile is even issued); selected below
+  // a folding row's raw k and v rows, after the verify's own regions
+  char* const Fs = lds + verify_lds_bytes<IT, V, K, MF>(T, L);
+  if constexpr (FL) {
+    if (wf > 0) {
+      dma_rows(Fs, 0, wf * QV, (const char*)a.k_ring + kring0 * kIo, wave, lane, NT);
+      dma_rows(Fs, L * QV, wf * VV, (const char*)a.v_ring + dring0 * kIo, wave, lane, NT);
+    }
+  }
+  // gates: committed (or folded) entries from the ring, the drafts from the
+  // inputs, all loaded by clamped indices (a load in a branch would make the
+  // compiler wait for every staged row before the tile is even issued);
+  // selected below
   const int td = lane - w < 0 ? 0 : (lane - w < T ? lane - w : T - 1);
-  const float g_ring_l = a.g_ring[gring0 + (lane < w ? lane : 0)];
+  const float g_ring_l = a.g_ring[gring0 + (lane < w_in ? lane : 0)];
+  const float b_ring_l = FL ? a.beta_ring[gring0 + (lane < wf ? lane : 0)] : 0.f;
   const float g_new_l = a.g[(long)(b * T + td) * HV + hv];
   const float b_new_l = a.beta[(long)(b * T + (lane < T ? lane : T - 1)) * HV + hv];
   // the tile last: step 2 needs only the staged rows and the gates, so it
@@ -227,6 +379,18 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   __builtin_amdgcn_s_waitcnt((ITEMS & 15) | ((ITEMS >> 4) << 14));
   __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
+  if constexpr (FL) {
+    if (wf > 0) {
+      // fold ring entries 0..wf-1 into the tile (its loads are waited for at
+      // the first use), store it; the drafts then see the folded state
+      fold_steps_v<IT, V, K>(sv, Fs, Fs + (long)L * QV * 16,
+                             reinterpret_cast<float*>(Fs + (long)L * (QV + VV) * 16), g_ring_l,
+                             b_ring_l, wf, tid);
+#pragma unroll
+      for (int it = 0; it < ITEMS; ++it)
+        st16_stream(tptr, (long)lane_off + it * NT * 16, sv[it]);
+    }
+  }
   // gate of ring entry `lane` (committed entries, then the drafts); 1 past them
   const float gl = lane < w ? g_ring_l : (lane < w + T ? g_new_l : 1.f);
   const float bl = lane < T ? b_new_l : 0.f;
@@ -432,7 +596,9 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   // consecutive lanes with non-temporal stores (written this way, scattered
   // ring writes inside the tile read stream cost a third of the per-row
   // layout); then g and beta
-  const bool k_writer = (hv % a.vpk) == 0;
+  // (after a fold the other value heads of this key head may still be
+  // reading its old k rows: those rows are written by the advance instead)
+  const bool k_writer = (hv % a.vpk) == 0 && !fold;
   {
     const int nd = T * DV, nv = T * VV, nk = k_writer ? T * QV : 0;
     for (int e = tid; e < nd + nv + nk; e += NT) {
@@ -520,13 +686,6 @@ struct Reduce8 {
     return it;
   }
 };
-
-// The fold holds the tile as gam * S: a step's decay g multiplies the scalar
-// gam instead of every element, the row dot is gam * (S.k) and the rank-1
-// update adds (d / gam) k to S.  Algebraically the recurrence; when gam
-// would leave [2^-60, 2^60] (or g is 0 or not finite) the pending decay and
-// the step's own are applied to S element by element and gam restarts at 1.
-constexpr float kLazyFloor = 0x1p-60f, kLazyCeil = 0x1p60f;
 
 // The entry loop of a fold: this lane's rows S of the tile, entries 0..wn-1
 // in order (k rows as fp32 in K32, v rows as stored in Vs, g and beta of
@@ -787,32 +946,84 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_ke
   }
 }
 
+// Cursor advance of the deferred-fold rounds, one workgroup per row: a row
+// that folded in this round's verify starts from entry 0, then keeps its
+// accepted drafts (commit_row); the next verify folds it when the flag is
+// set.  A row that folded also receives its drafts' k rows at ring entries
+// 0..T-1 here, not in the verify, where other value heads of its key head
+// may still have been reading the old rows.  The k rows are loaded with the
+// row's cursor, before the flag is known, so the row costs one round trip.
+template <typename IT, int K>
+__global__ void __launch_bounds__(256) gdn_spec_advance_kernel(const SpecArgs a) {
+  constexpr int QV = K / Elt<IT>::kPer16;
+  constexpr int NT = 256, B = 4;
+  constexpr long kIo = sizeof(IT);
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int T = a.n_draft, L = a.ring_len, HK = a.k_heads;
+  const int n = HK * T * QV;  // k vectors of the row's drafts: [t, hk, K] in the input
+  const char* const ksrc = static_cast<const char*>(a.k) + (long)r * n * 16;
+  for (int u0 = 0; u0 < n; u0 += B * NT) {
+    u32x4 x[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int u = u0 + j * NT + tid;
+      x[j] = ld16(ksrc, (long)(u < n ? u : n - 1) * 16);  // clamped: no load in a branch
+    }
+    const int s = a.slot_idx[r];
+    const bool folded = a.is_flush[r] != 0;
+    if (u0 == 0 && tid == 0) {
+      const CommitRow cr = commit_row(s, folded ? 0 : a.write_pos[r], a.accepted[r],
+                                      a.force_flush && a.force_flush[r], a);
+      a.next_write_pos[r] = cr.wn;
+      a.next_is_flush[r] = cr.flush ? 1 : 0;
+      if (cr.st && a.status) atomicOr(a.status, cr.st);
+    }
+    if (!folded || s < 0 || s >= a.num_slots) return;
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int u = u0 + j * NT + tid;
+      if (u < n) {
+        const int t = u / (HK * QV);
+        const int hk = (u - t * HK * QV) / QV;
+        const int c = u - (t * HK + hk) * QV;
+        st16(a.k_ring, ((((long)s * HK + hk) * L + t) * K) * kIo + (long)c * 16, x[j]);
+      }
+    }
+  }
+}
+
 // bf16 inputs at V = K = 128 take the matrix-core products when the extra
 // LDS fits; otherwise (fp32 inputs, other shapes, the largest rings) the
 // vector path.
-template <typename IT, typename OT, int V, int K, int TM>
+template <typename IT, typename OT, int V, int K, int TM, bool FL>
 static int launch_verify_tm(const SpecArgs& a, int batch, hipStream_t stream) {
-  using SG = VerifyStage<IT, V, K>;
   constexpr int NT = GdnShape<V, K, true>::NT;
   const size_t fixed = (2 * TM * 64 + TM) * sizeof(float);
   const unsigned grid = (unsigned)((long)batch * a.v_heads);
-  const size_t lds = (size_t)SG::chunks(a.n_draft, a.ring_len) * 16;
+  // a folding row stages its raw ring rows after the verify's regions
+  const size_t fold = FL ? verify_fold_bytes<IT, V, K>(a.ring_len) : 0;
   if constexpr (std::is_same<IT, bf16>::value && V == 128 && K == 128 && NT == 256) {
-    if (lds + VerifyMfma::kBytes + fixed <= kMaxLds)
+    const size_t lds = verify_lds_bytes<IT, V, K, true>(a.n_draft, a.ring_len) + fold;
+    if (lds + fixed <= kMaxLds)
       return launch_kernel(
-          reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, true, TM>), grid,
-          NT, lds + VerifyMfma::kBytes, stream, a);
+          reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, true, TM, FL>),
+          grid, NT, lds, stream, a);
   }
+  const size_t lds = verify_lds_bytes<IT, V, K, false>(a.n_draft, a.ring_len) + fold;
   if (lds + fixed > kMaxLds) return RSSM_ESHAPE;  // staged rows must fit one workgroup's LDS
   return launch_kernel(
-      reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, false, TM>), grid, NT,
-      lds, stream, a);
+      reinterpret_cast<const void*>(&gdn_spec_verify_kernel<IT, OT, V, K, false, TM, FL>), grid,
+      NT, lds, stream, a);
 }
 
 template <typename IT, typename OT, int V, int K>
 static int launch_verify(const SpecArgs& a, int batch, hipStream_t stream) {
-  return a.n_draft <= 4 ? launch_verify_tm<IT, OT, V, K, 4>(a, batch, stream)
-                        : launch_verify_tm<IT, OT, V, K, kMaxDraft>(a, batch, stream);
+  if (a.is_flush)
+    return a.n_draft <= 4 ? launch_verify_tm<IT, OT, V, K, 4, true>(a, batch, stream)
+                          : launch_verify_tm<IT, OT, V, K, kMaxDraft, true>(a, batch, stream);
+  return a.n_draft <= 4 ? launch_verify_tm<IT, OT, V, K, 4, false>(a, batch, stream)
+                        : launch_verify_tm<IT, OT, V, K, kMaxDraft, false>(a, batch, stream);
 }
 
 // Grid of the task-list commit: enough resident workgroups to keep every CU
@@ -847,6 +1058,13 @@ static int commit_shape(const SpecArgs& a, const rssm_gdn_dims& d, hipStream_t s
   return RSSM_ESHAPE;
 }
 
+template <typename IT>
+static int launch_advance(const SpecArgs& a, const rssm_gdn_dims& d, hipStream_t s) {
+  const void* fn = d.dk == 128 ? reinterpret_cast<const void*>(&gdn_spec_advance_kernel<IT, 128>)
+                               : reinterpret_cast<const void*>(&gdn_spec_advance_kernel<IT, 64>);
+  return launch_kernel(fn, (unsigned)d.batch, 256, 0, s, a);
+}
+
 static int spec_check(const rssm_gdn_dims* d, int32_t n_draft) {
   if (!d) return RSSM_EINVAL;
   if (d->batch < 0 || d->k_heads < 1 || d->v_heads < 1 || d->v_heads % d->k_heads ||
@@ -877,13 +1095,12 @@ static SpecArgs spec_args(const rssm_gdn_dims* d, int32_t n_draft) {
 
 using namespace rssm;
 
-extern "C" int replayssm_gdn_spec_verify(const rssm_gdn_dims* dims, int32_t n_draft,
-                                         const void* state, float* d_ring, void* k_ring,
-                                         float* g_ring, void* v_ring, float* beta_ring,
-                                         const int32_t* slot_idx, const int32_t* write_pos,
-                                         const void* q, const void* k, const void* v,
-                                         const float* g, const float* beta, void* o,
-                                         int32_t* status, hipStream_t stream) {
+static int spec_verify(const rssm_gdn_dims* dims, int32_t n_draft, const void* state,
+                       float* d_ring, void* k_ring, float* g_ring, void* v_ring,
+                       float* beta_ring, const int32_t* slot_idx, const int32_t* write_pos,
+                       const uint8_t* is_flush, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, void* o, int32_t* status,
+                       hipStream_t stream) {
   int rc = spec_check(dims, n_draft);
   if (rc) return rc;
   if (dims->batch == 0) return RSSM_OK;
@@ -894,6 +1111,7 @@ extern "C" int replayssm_gdn_spec_verify(const rssm_gdn_dims* dims, int32_t n_dr
       !aligned16(q) || !aligned16(k) || !aligned16(v))
     return RSSM_EINVAL;
   SpecArgs a = spec_args(dims, n_draft);
+  a.is_flush = is_flush;
   a.state = const_cast<float*>(static_cast<const float*>(state));
   a.d_ring = d_ring;
   a.k_ring = k_ring;
@@ -914,6 +1132,64 @@ extern "C" int replayssm_gdn_spec_verify(const rssm_gdn_dims* dims, int32_t n_dr
     case 1: return verify_shape<float, bf16>(a, *dims, stream);
     case 2: return verify_shape<bf16, float>(a, *dims, stream);
     case 3: return verify_shape<bf16, bf16>(a, *dims, stream);
+  }
+  return RSSM_EDTYPE;
+}
+
+extern "C" int replayssm_gdn_spec_verify(const rssm_gdn_dims* dims, int32_t n_draft,
+                                         const void* state, float* d_ring, void* k_ring,
+                                         float* g_ring, void* v_ring, float* beta_ring,
+                                         const int32_t* slot_idx, const int32_t* write_pos,
+                                         const void* q, const void* k, const void* v,
+                                         const float* g, const float* beta, void* o,
+                                         int32_t* status, hipStream_t stream) {
+  return spec_verify(dims, n_draft, state, d_ring, k_ring, g_ring, v_ring, beta_ring, slot_idx,
+                     write_pos, nullptr, q, k, v, g, beta, o, status, stream);
+}
+
+extern "C" int replayssm_gdn_spec_verify_flush(
+    const rssm_gdn_dims* dims, int32_t n_draft, float* state, float* d_ring, void* k_ring,
+    float* g_ring, void* v_ring, float* beta_ring, const int32_t* slot_idx,
+    const int32_t* write_pos, const uint8_t* is_flush, const void* q, const void* k,
+    const void* v, const float* g, const float* beta, void* o, int32_t* status,
+    hipStream_t stream) {
+  if (!is_flush && dims && dims->batch > 0) return RSSM_EINVAL;
+  return spec_verify(dims, n_draft, state, d_ring, k_ring, g_ring, v_ring, beta_ring, slot_idx,
+                     write_pos, is_flush, q, k, v, g, beta, o, status, stream);
+}
+
+extern "C" int replayssm_gdn_spec_advance(const rssm_gdn_dims* dims, int32_t n_draft,
+                                          void* k_ring, const void* k,
+                                          const int32_t* slot_idx, const int32_t* write_pos,
+                                          const uint8_t* is_flush, const int32_t* accepted,
+                                          const uint8_t* force_flush, int32_t* next_write_pos,
+                                          uint8_t* next_is_flush, int32_t* status,
+                                          hipStream_t stream) {
+  int rc = spec_check(dims, n_draft);
+  if (rc) return rc;
+  if (dims->batch == 0) return RSSM_OK;
+  if (!k_ring || !k || !slot_idx || !write_pos || !is_flush || !accepted || !next_write_pos ||
+      !next_is_flush)
+    return RSSM_EINVAL;
+  if (!aligned16(k_ring) || !aligned16(k)) return RSSM_EINVAL;
+  if ((const void*)next_write_pos == (const void*)write_pos ||
+      (const void*)next_is_flush == (const void*)is_flush)
+    return RSSM_EINVAL;
+  SpecArgs a = spec_args(dims, n_draft);
+  a.k_ring = k_ring;
+  a.k = k;
+  a.slot_idx = slot_idx;
+  a.write_pos = write_pos;
+  a.is_flush = is_flush;
+  a.accepted = accepted;
+  a.force_flush = force_flush;
+  a.next_write_pos = next_write_pos;
+  a.next_is_flush = next_is_flush;
+  a.status = status;
+  a.n_rows = dims->batch;
+  switch (dims->io_dtype) {
+    case RSSM_F32: return launch_advance<float>(a, *dims, stream);
+    case RSSM_BF16: return launch_advance<bf16>(a, *dims, stream);
   }
   return RSSM_EDTYPE;
 }

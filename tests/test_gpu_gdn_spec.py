@@ -168,6 +168,201 @@ def test_spec_commit_large_batch_and_unaligned_cursors():
     run_spec(40, 2, 4, 128, 128, 16, 4, torch.bfloat16, 10, range(0, 40, 7), seed=92, offset=1)
 
 
+def run_spec_deferred(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32,
+                      gates=None, force_p=0.1):
+    """Deferred-fold rounds (verify with flush, then advance) on the GPU
+    against the oracle's eager rounds (verify, then commit with its fold) on
+    the same inputs: the drafts' outputs agree every round; a row's fold,
+    done by the GPU at its next verify, leaves the state the oracle's commit
+    left; the cursors follow the advance rule and agree with the oracle's
+    (w' where the oracle kept it, 0 where it folded); a folded row's new
+    k rows land at its ring entries 0..T-1; at the end every sampled row's
+    checkpoint folded with its ring equals the oracle's."""
+    print(f"case: deferred spec nb={nb} HK={HK} HV={HV} K={K} V={V} L={L} T={T} io={io}",
+          flush=True)
+    rng = np.random.default_rng(seed)
+    dev = torch.device("cuda:0")
+    ns = nb + 3
+    slots = rng.permutation(ns)[:nb].astype(np.int32)
+    pool = rng.normal(0, 0.1, (ns, HV, V, K)).astype(np.float32)
+    st = torch.tensor(pool, device=dev)
+    dr = torch.full((ns, HV, L, V), float("nan"), device=dev)
+    kr = torch.full((ns, HK, L, K), float("nan"), dtype=io, device=dev)
+    gr = torch.full((ns, HV, L), float("nan"), device=dev)
+    vr = torch.full((ns, HV, L, V), float("nan"), dtype=io, device=dev)
+    br = torch.full((ns, HV, L), float("nan"), device=dev)
+    wp = torch.zeros(nb, dtype=torch.int32, device=dev)
+    nwp = torch.zeros(nb, dtype=torch.int32, device=dev)
+    fl = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    nfl = torch.zeros(nb, dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    sl = torch.tensor(slots, device=dev)
+    sample = sorted(set(sample))
+    k_ = len(sample)
+    o_pool = pool[slots[sample]].astype(np.float64)
+    o_rings = [np.full((k_, HV, L, V), np.nan), np.full((k_, HK, L, K), np.nan),
+               np.full((k_, HV, L), np.nan), np.full((k_, HV, L, V), np.nan),
+               np.full((k_, HV, L), np.nan)]
+    o_sl = np.arange(k_)
+    o_wp = np.zeros(k_, np.int32)
+    fp32 = io == torch.float32
+    lim = (lambda ref: 2e-5 * np.abs(ref).max()) if fp32 else (lambda ref: 1e-2)
+    folds = 0
+    for r in range(rounds):
+        q = torch.tensor(_unit(rng, (nb, T, HK, K)), dtype=io, device=dev)
+        k = torch.tensor(_unit(rng, (nb, T, HK, K)), dtype=io, device=dev)
+        v = torch.tensor(rng.normal(size=(nb, T, HV, V)), dtype=io, device=dev)
+        gv = (gates(rng, (nb, T, HV)) if gates else
+              np.exp(-np.log1p(np.exp(rng.normal(size=(nb, T, HV))))))
+        g = torch.tensor(gv, dtype=torch.float32, device=dev)
+        beta = torch.tensor(1 / (1 + np.exp(-rng.normal(size=(nb, T, HV)))),
+                            dtype=torch.float32, device=dev)
+        fl_now = fl.cpu().numpy().astype(bool)
+        wp_now = wp.cpu().numpy()
+        o = R.replayssm_gdn_spec_verify_flush(st, dr, kr, gr, vr, br, sl, wp, fl, q, k, v, g,
+                                              beta, status=status, out_dtype=out)
+        # a folding row's stored state is the oracle's state after its last commit
+        for j, row in enumerate(sample):
+            if fl_now[row] and wp_now[row] > 0:
+                folds += 1
+                gs = st[int(slots[row])].double().cpu().numpy()
+                e = np.abs(gs - o_pool[j]).max()
+                assert e <= lim(o_pool[j]), f"round {r} row {row}: folded state error {e:.2e}"
+        npv = lambda t: t[sample].double().cpu().numpy()
+        o_ref, ost = OS.gdn_spec_verify(o_pool, *o_rings, o_sl, o_wp, npv(q), npv(k), npv(v),
+                                        npv(g), npv(beta))
+        assert ost == 0
+        got = o[sample].double().cpu().numpy()
+        d = np.abs(got - o_ref)
+        if fp32 and out == torch.float32:
+            err = d.max() / np.abs(o_ref).max()
+            assert err <= 2e-5, f"round {r}: o error {err:.2e}"
+        else:
+            bound = np.maximum(1e-2, np.abs(o_ref) * 2**-7)
+            assert (d <= bound).all(), f"round {r}: o error {d.max():.2e}"
+        acc = rng.integers(0, T + 1, nb).astype(np.int32)
+        force = (rng.random(nb) < force_p).astype(np.uint8)
+        R.replayssm_gdn_spec_advance(kr, sl, wp, fl, torch.tensor(acc, device=dev), T, k, nwp,
+                                     nfl, force_flush=torch.tensor(force, device=dev),
+                                     status=status)
+        o_wp, o_fl, ost = OS.gdn_spec_commit(o_pool, *o_rings[1:], o_sl, o_wp, acc[sample], T,
+                                             force_flush=force[sample], state_dtype="f32")
+        assert ost == 0
+        w_all = np.where(fl_now, 0, wp_now) + acc
+        nfl_ref = ((w_all + T > L) | (force != 0)).astype(np.uint8)
+        np.testing.assert_array_equal(nwp.cpu().numpy(), w_all)
+        np.testing.assert_array_equal(nfl.cpu().numpy(), nfl_ref)
+        np.testing.assert_array_equal(o_fl, nfl_ref[sample])
+        np.testing.assert_array_equal(o_wp, np.where(nfl_ref, 0, w_all)[sample])
+        # the drafts' k rows of rows that folded this round, written by the advance
+        krs = kr.cpu()
+        for row in np.flatnonzero(fl_now):
+            got_k = krs[int(slots[row]), :, :T, :]
+            want_k = k[row].cpu().permute(1, 0, 2)
+            assert torch.equal(got_k.view(torch.int16) if io == torch.bfloat16 else got_k,
+                               want_k.view(torch.int16) if io == torch.bfloat16 else want_k)
+        wp, nwp = nwp, wp
+        fl, nfl = nfl, fl
+    torch.cuda.synchronize()
+    assert status.item() == 0
+    assert folds > 0
+    # end: each sampled row's logical state (checkpoint folded with its ring)
+    rings = [t.double().cpu().numpy() for t in (kr, gr, vr, br)]
+    wpe = wp.cpu().numpy()
+    kh = np.arange(HV) // (HV // HK)
+    for j, row in enumerate(sample):
+        s = int(slots[row])
+        got = OS.exact_fold(st[s].double().cpu().numpy(), *rings, s, int(wpe[row]), kh)
+        ref = OS.exact_fold(o_pool[j], o_rings[1], o_rings[2], o_rings[3], o_rings[4], j,
+                            int(o_wp[j]), kh)
+        e = np.abs(got - ref).max()
+        assert e <= lim(ref), f"row {row}: end state error {e:.2e}"
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64), (64, 128), (128, 64)])
+def test_spec_deferred_small(io, K, V):
+    run_spec_deferred(5, 2, 4, K, V, 8, 3, io, 14, range(5), seed=K + V + 7)
+
+
+@pytest.mark.parametrize("L,T,io", [(2, 1, torch.bfloat16), (16, 8, torch.bfloat16),
+                                    (20, 5, torch.bfloat16), (35, 8, torch.bfloat16),
+                                    (42, 8, torch.bfloat16), (46, 4, torch.bfloat16),
+                                    (24, 8, torch.float32), (27, 4, torch.float32)])
+def test_spec_deferred_ring_lengths(L, T, io):
+    """Up to the longest rings whose raw rows fit beside the verify's staging
+    (42 / 46 entries with bf16 inputs, 24 / 27 with fp32; 35 is the longest
+    on the matrix-core path at 8 drafts)."""
+    run_spec_deferred(3, 1, 2, 128, 128, L, T, io, max(6, 3 * L // T), range(3), seed=L * 5 + T)
+
+
+def test_spec_deferred_full_size_bf16_output():
+    """256 rows, 16 key / 32 value heads, K = V = 128, L = 16, 4 drafts."""
+    run_spec_deferred(256, 16, 32, 128, 128, 16, 4, torch.bfloat16, 12, [0, 99, 200, 255],
+                      seed=14, out=torch.bfloat16)
+
+
+@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
+def test_spec_deferred_fold_with_extreme_decays(io):
+    L = 32 if io == torch.bfloat16 else 24
+    run_spec_deferred(6, 2, 4, 128, 128, L, 8, io, 20, range(6), seed=195, gates=_extreme_gates)
+    run_spec_deferred(6, 1, 2, 64, 128, 16, 4, io, 16, range(6), seed=196, gates=_extreme_gates)
+
+
+def test_spec_deferred_every_row_folds():
+    """Every advance forced: every row folds in every verify."""
+    run_spec_deferred(256, 16, 32, 128, 128, 16, 4, torch.bfloat16, 4, [0, 77, 200, 255],
+                      seed=197, force_p=1.0)
+
+
+def test_spec_deferred_too_long_ring_is_refused():
+    print("case: deferred spec ring too long", flush=True)
+    dev = torch.device("cuda:0")
+    HK, HV, K, V, L, T = 1, 2, 128, 128, 47, 4
+    st = torch.zeros((2, HV, V, K), device=dev)
+    rings = (torch.zeros((2, HV, L, V), device=dev),
+             torch.zeros((2, HK, L, K), dtype=torch.bfloat16, device=dev),
+             torch.zeros((2, HV, L), device=dev),
+             torch.zeros((2, HV, L, V), dtype=torch.bfloat16, device=dev),
+             torch.zeros((2, HV, L), device=dev))
+    sl = torch.tensor([0, 1], dtype=torch.int32, device=dev)
+    wp = torch.zeros(2, dtype=torch.int32, device=dev)
+    fl = torch.zeros(2, dtype=torch.uint8, device=dev)
+    q = torch.ones((2, T, HK, K), dtype=torch.bfloat16, device=dev)
+    v = torch.ones((2, T, HV, V), dtype=torch.bfloat16, device=dev)
+    gb = torch.full((2, T, HV), 0.5, device=dev)
+    with pytest.raises(R.RssmError):
+        R.replayssm_gdn_spec_verify_flush(st, *rings, sl, wp, fl, q, q, v, gb, gb)
+    # the verify without folds still takes it
+    R.replayssm_gdn_spec_verify(st, *rings, sl, wp, q, q, v, gb, gb)
+    torch.cuda.synchronize()
+
+
+def test_spec_deferred_bad_cursor_is_refused():
+    """A folding row past the ring (w > L) and an other row whose drafts do
+    not fit (w + T > L) are refused with the status bit and NaN outputs;
+    the good rows are verified."""
+    print("case: deferred spec bad cursors", flush=True)
+    dev = torch.device("cuda:0")
+    HK, HV, K, V, L, T = 1, 2, 64, 64, 8, 4
+    st = torch.zeros((4, HV, V, K), device=dev)
+    rings = tuple(torch.zeros(sh, device=dev) for sh in
+                  ((4, HV, L, V), (4, HK, L, K), (4, HV, L), (4, HV, L, V), (4, HV, L)))
+    sl = torch.tensor([0, 1, 2, 3], dtype=torch.int32, device=dev)
+    wp = torch.tensor([0, 9, 5, 8], dtype=torch.int32, device=dev)
+    fl = torch.tensor([0, 1, 0, 1], dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    q = torch.ones((4, T, HK, K), device=dev) / 8
+    v = torch.ones((4, T, HV, V), device=dev)
+    gb = torch.full((4, T, HV), 0.5, device=dev)
+    o = R.replayssm_gdn_spec_verify_flush(st, *rings, sl, wp, fl, q, q, v, gb, gb,
+                                          status=status)
+    torch.cuda.synchronize()
+    assert status.item() & R.ST_RING_OVERFLOW
+    assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all()
+    assert torch.isfinite(o[0]).all() and torch.isfinite(o[3]).all()
+
+
 def test_spec_bad_cursor_is_refused():
     print("case: spec bad cursor", flush=True)
     dev = torch.device("cuda:0")

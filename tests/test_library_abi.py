@@ -86,6 +86,27 @@ def test_host_validation_rejects_bad_arguments_without_a_gpu():
                                          V(0x2000), None, None, None) == -1        # no accepted
     assert lib.replayssm_gdn_spec_commit(ctypes.byref(gd), 4, *cm, V(0x3000), V(0x1000), None,
                                          V(0x3000), None, None, None) == -1        # aliasing
+    # deferred-fold rounds: is_flush is required; a folding row's raw ring
+    # rows must fit beside the verify's staging (46 entries at T = 4, bf16)
+    P = V(0x1000)
+    fv = [P] * 8                              # state .. write_pos
+    gd = R.GdnDims(2, 1, 2, 128, 128, 16, 4, 0, 1, 1, 0.0)
+    assert lib.replayssm_gdn_spec_verify_flush(ctypes.byref(gd), 4, *fv, None, *[P] * 6,
+                                               None, None) == -1
+    for L, io in ((47, 1), (28, 0)):         # past 46 (bf16) / 27 (fp32) entries
+        gd = R.GdnDims(2, 1, 2, 128, 128, L, 4, 0, io, 1, 0.0)
+        assert lib.replayssm_gdn_spec_verify_flush(ctypes.byref(gd), 4, *fv, P, *[P] * 6,
+                                                   None, None) == -4
+    gd = R.GdnDims(2, 1, 2, 128, 128, 16, 4, 0, 1, 1, 0.0)
+    A, B = V(0x2000), V(0x3000)
+    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, P, P, P, P, A, P, None, B, A,
+                                          None, None) == -1        # next_is_flush aliases is_flush
+    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, P, P, P, B, A, P, None, B, P,
+                                          None, None) == -1        # next_write_pos aliases write_pos
+    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, P, P, P, P, A, None, None, B, P,
+                                          None, None) == -1        # no accepted
+    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, P, V(0x1008), P, P, A, P, None,
+                                          B, P, None, None) == -1  # misaligned k
     # KDA: the gate rows are vector operands (16-byte alignment) and take LDS
     # of their own (at K = V = 128 a ring fits 48 entries with bf16 inputs)
     P = V(0x1000)
