@@ -41,6 +41,16 @@
 // are sums over eight lanes by DPP, d passes within the wave through LDS,
 // then the rank-1 update (the waves never wait for one another); the tile is
 // stored scaled by the product.
+//
+// Deferred-fold rounds: the commit only advances the cursors and marks the
+// rows whose next verify would not fit (a per-row is_flush flag); that
+// verify folds their ring on the tile registers it has just loaded (the
+// same recurrence on the verify's lane layout, row sums over 16 or 32 lanes
+// by row swaps and DPP), stores the folded tile and verifies the drafts at
+// entries 0..T-1, so the folding tile is read from memory once instead of
+// twice.  The drafts' k rows of such a row are written by the advance: in
+// the verify the other value heads of the key head may still be reading
+// the old ones for their own folds.
 #include <math.h>
 
 #include "gdn_common.hpp"
@@ -951,8 +961,7 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_ke
 // accepted drafts (commit_row); the next verify folds it when the flag is
 // set.  A row that folded also receives its drafts' k rows at ring entries
 // 0..T-1 here, not in the verify, where other value heads of its key head
-// may still have been reading the old rows.  The k rows are loaded with the
-// row's cursor, before the flag is known, so the row costs one round trip.
+// may still have been reading the old rows.
 template <typename IT, int K>
 __global__ void __launch_bounds__(256) gdn_spec_advance_kernel(const SpecArgs a) {
   constexpr int QV = K / Elt<IT>::kPer16;
@@ -961,7 +970,19 @@ __global__ void __launch_bounds__(256) gdn_spec_advance_kernel(const SpecArgs a)
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int T = a.n_draft, L = a.ring_len, HK = a.k_heads;
-  const int n = HK * T * QV;  // k vectors of the row's drafts: [t, hk, K] in the input
+  const int s = a.slot_idx[r];
+  const bool folded = a.is_flush[r] != 0;
+  if (tid == 0) {
+    const CommitRow cr = commit_row(s, folded ? 0 : a.write_pos[r], a.accepted[r],
+                                    a.force_flush && a.force_flush[r], a);
+    a.next_write_pos[r] = cr.wn;
+    a.next_is_flush[r] = cr.flush ? 1 : 0;
+    if (cr.st && a.status) atomicOr(a.status, cr.st);
+  }
+  if (!folded || s < 0 || s >= a.num_slots) return;
+  // k rows of the T drafts: input [row, t, hk, K] -> ring [s, hk, t, K], in
+  // batches of B vectors per thread, every load of a batch before its stores
+  const int n = HK * T * QV;
   const char* const ksrc = static_cast<const char*>(a.k) + (long)r * n * 16;
   for (int u0 = 0; u0 < n; u0 += B * NT) {
     u32x4 x[B];
@@ -970,16 +991,6 @@ __global__ void __launch_bounds__(256) gdn_spec_advance_kernel(const SpecArgs a)
       const int u = u0 + j * NT + tid;
       x[j] = ld16(ksrc, (long)(u < n ? u : n - 1) * 16);  // clamped: no load in a branch
     }
-    const int s = a.slot_idx[r];
-    const bool folded = a.is_flush[r] != 0;
-    if (u0 == 0 && tid == 0) {
-      const CommitRow cr = commit_row(s, folded ? 0 : a.write_pos[r], a.accepted[r],
-                                      a.force_flush && a.force_flush[r], a);
-      a.next_write_pos[r] = cr.wn;
-      a.next_is_flush[r] = cr.flush ? 1 : 0;
-      if (cr.st && a.status) atomicOr(a.status, cr.st);
-    }
-    if (!folded || s < 0 || s >= a.num_slots) return;
 #pragma unroll
     for (int j = 0; j < B; ++j) {
       const int u = u0 + j * NT + tid;
