@@ -63,3 +63,11 @@ def test_gdn_spec_long_run_through_exact_folds():
     folded state against the oracle."""
     from test_gpu_gdn_spec import run_spec
     run_spec(4, 2, 4, 128, 128, 16, 4, torch.bfloat16, 400, range(4), seed=4300)
+
+
+def test_gdn_spec_deferred_long_run_through_exact_folds():
+    """The deferred-fold rounds over the same 400-round schedule: each fold
+    runs in the next verify, on the tile it loads; draft outputs every round
+    and the folded states against the oracle's eager rounds."""
+    from test_gpu_gdn_spec import run_spec_deferred
+    run_spec_deferred(4, 2, 4, 128, 128, 16, 4, torch.bfloat16, 400, range(4), seed=4300)

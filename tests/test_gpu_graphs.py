@@ -223,3 +223,71 @@ def test_gdn_spec_rounds_in_a_graph():
 
     _check_replays(lambda k: rnd(lay["eager"], k), lambda k: rnd(lay["graph"], k), k_rounds,
                    snapshot, dev)
+
+
+def test_gdn_spec_deferred_rounds_in_a_graph():
+    """Deferred-fold rounds (verify with flush + advance: the fold flags and
+    the cursors ping-pong), 4 rounds per graph, some rows forced to fold."""
+    wl = GdnWorkload("graph_spec_def", 8, 2, 4, 128, 128, 16, 4, 12, "bf16", "f32", 4600)
+    gen = GdnInputs(wl)
+    dev = torch.device("cuda:0")
+    print("case: gdn deferred spec rounds, 4 rounds per graph", flush=True)
+    HK, HV, K, V, L, ns, nb = (wl.k_heads, wl.v_heads, wl.dk, wl.dv, wl.ring_len, wl.num_slots,
+                               wl.batch)
+    T, k_rounds = 4, 4
+    io = TORCH_DTYPES[wl.io_dtype]
+    g0 = torch.Generator().manual_seed(4600)
+
+    def unit(shape):
+        a = torch.randn(shape, generator=g0)
+        return (a / a.norm(dim=-1, keepdim=True)).to(io).to(dev)
+
+    def normal(shape):
+        return torch.randn(shape, generator=g0).to(io).to(dev)
+
+    inps = []
+    for _ in range(k_rounds):
+        gate = torch.randn((nb, T, HV), generator=g0)
+        inps.append({"q": unit((nb, T, HK, K)), "k": unit((nb, T, HK, K)),
+                     "v": normal((nb, T, HV, V)),
+                     "g": torch.exp(-torch.nn.functional.softplus(gate)).to(dev),
+                     "beta": torch.sigmoid(torch.randn((nb, T, HV), generator=g0)).to(dev),
+                     "acc": torch.randint(0, T + 1, (nb,), generator=g0, dtype=torch.int32).to(dev),
+                     "force": (torch.rand(nb, generator=g0) < 0.2).to(torch.uint8).to(dev)})
+
+    def layer():
+        return {"state": gen.state_pool().to(dev),
+                "dr": torch.zeros((ns, HV, L, V), device=dev),
+                "kr": torch.zeros((ns, HK, L, K), dtype=io, device=dev),
+                "gr": torch.zeros((ns, HV, L), device=dev),
+                "vr": torch.zeros((ns, HV, L, V), dtype=io, device=dev),
+                "br": torch.zeros((ns, HV, L), device=dev),
+                "wp": torch.zeros(nb, dtype=torch.int32, device=dev),
+                "nwp": torch.zeros(nb, dtype=torch.int32, device=dev),
+                "fl": torch.zeros(nb, dtype=torch.uint8, device=dev),
+                "nfl": torch.zeros(nb, dtype=torch.uint8, device=dev),
+                "o": [torch.empty((nb, T, HV, V), dtype=io, device=dev) for _ in range(k_rounds)]}
+
+    slots = gen.slot_idx().to(dev)
+    lay = {"eager": layer(), "graph": layer()}
+
+    def rnd(d, k):
+        x = inps[k]
+        R.replayssm_gdn_spec_verify_flush(d["state"], d["dr"], d["kr"], d["gr"], d["vr"],
+                                          d["br"], slots, d["wp"], d["fl"], x["q"], x["k"],
+                                          x["v"], x["g"], x["beta"], o=d["o"][k])
+        R.replayssm_gdn_spec_advance(d["kr"], slots, d["wp"], d["fl"], x["acc"], T, x["k"],
+                                     d["nwp"], d["nfl"], force_flush=x["force"])
+        d["wp"], d["nwp"] = d["nwp"], d["wp"]
+        d["fl"], d["nfl"] = d["nfl"], d["fl"]
+
+    def snapshot(which):
+        d = lay[which]
+        out = {f"o{k}": d["o"][k].clone() for k in range(k_rounds)}
+        out.update(state=d["state"].clone(), wp=d["wp"].clone(), fl=d["fl"].clone(),
+                   dr=d["dr"].clone(), kr=d["kr"].clone(), gr=d["gr"].clone(),
+                   vr=d["vr"].clone(), br=d["br"].clone())
+        return out
+
+    _check_replays(lambda k: rnd(lay["eager"], k), lambda k: rnd(lay["graph"], k), k_rounds,
+                   snapshot, dev)
