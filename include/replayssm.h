@@ -373,7 +373,12 @@ int replayssm_gdn_spec_commit(const rssm_gdn_dims* dims, int32_t n_draft, void* 
  * rounds a row's logical state is its checkpoint folded with ring entries
  * 0..write_pos-1, and is_flush marks rows whose next verify folds first.
  * Cursors start at write_pos = 0, is_flush = 0.  A row keeps to one kind of
- * round (a pending fold is not visible to replayssm_gdn_spec_verify).
+ * round (a pending fold is not visible to replayssm_gdn_spec_verify).  To
+ * empty a row's ring at once (before copying its slot, say),
+ * replayssm_gdn_spec_commit with accepted = 0 and force_flush set folds its
+ * entries 0..write_pos-1 and returns write_pos 0; then clear its is_flush.
+ * A row the verify refused (status bit) is left unspecified by the advance,
+ * which cannot tell that no fold took place.
  *
  * replayssm_gdn_spec_verify_flush - rows with is_flush[b] != 0 (is_flush
  * [batch] uint8, required) first fold ring entries 0..write_pos[b]-1 into

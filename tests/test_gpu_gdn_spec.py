@@ -169,7 +169,7 @@ def test_spec_commit_large_batch_and_unaligned_cursors():
 
 
 def run_spec_deferred(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torch.float32,
-                      gates=None, force_p=0.1):
+                      gates=None, force_p=0.1, drain=False):
     """Deferred-fold rounds (verify with flush, then advance) on the GPU
     against the oracle's eager rounds (verify, then commit with its fold) on
     the same inputs: the drafts' outputs agree every round; a row's fold,
@@ -177,7 +177,9 @@ def run_spec_deferred(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torc
     left; the cursors follow the advance rule and agree with the oracle's
     (w' where the oracle kept it, 0 where it folded); a folded row's new
     k rows land at its ring entries 0..T-1; at the end every sampled row's
-    checkpoint folded with its ring equals the oracle's."""
+    checkpoint folded with its ring equals the oracle's.  drain: then fold
+    every row's ring at once by the eager commit (no accepted drafts,
+    forced) and compare the stored states."""
     print(f"case: deferred spec nb={nb} HK={HK} HV={HV} K={K} V={V} L={L} T={T} io={io}",
           flush=True)
     rng = np.random.default_rng(seed)
@@ -277,6 +279,20 @@ def run_spec_deferred(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torc
                             int(o_wp[j]), kh)
         e = np.abs(got - ref).max()
         assert e <= lim(ref), f"row {row}: end state error {e:.2e}"
+        if drain:
+            o_pool[j] = ref
+    if drain:
+        zero = torch.zeros(nb, dtype=torch.int32, device=dev)
+        ones = torch.ones(nb, dtype=torch.uint8, device=dev)
+        R.replayssm_gdn_spec_commit(st, kr, gr, vr, br, sl, wp, zero, T, nwp, force_flush=ones,
+                                    status=status)
+        torch.cuda.synchronize()
+        assert status.item() == 0
+        assert (nwp.cpu().numpy() == 0).all()
+        for j, row in enumerate(sample):
+            got = st[int(slots[row])].double().cpu().numpy()
+            e = np.abs(got - o_pool[j]).max()
+            assert e <= lim(o_pool[j]), f"row {row}: drained state error {e:.2e}"
 
 
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
@@ -297,9 +313,17 @@ def test_spec_deferred_ring_lengths(L, T, io):
 
 
 def test_spec_deferred_full_size_bf16_output():
-    """256 rows, 16 key / 32 value heads, K = V = 128, L = 16, 4 drafts."""
+    """256 rows, 16 key / 32 value heads, K = V = 128, L = 16, 4 drafts; at
+    the end every ring is folded at once by the eager commit."""
     run_spec_deferred(256, 16, 32, 128, 128, 16, 4, torch.bfloat16, 12, [0, 99, 200, 255],
-                      seed=14, out=torch.bfloat16)
+                      seed=14, out=torch.bfloat16, drain=True)
+
+
+def test_spec_deferred_large_batch():
+    """520 rows (one advance workgroup per row; the verify's grid in batch
+    order), fp32 inputs, drained at the end."""
+    run_spec_deferred(520, 1, 2, 64, 64, 8, 3, torch.float32, 8, [0, 255, 300, 519], seed=93,
+                      drain=True)
 
 
 @pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
