@@ -412,16 +412,20 @@ def bench_gdn_spec(wl, T, layers, rounds, warmup, dev, reps, deferred=False):
                                               d["br"], slots, d["wp"], d["fl"], inp_i["q"],
                                               inp_i["k"], inp_i["v"], inp_i["g"], inp_i["beta"],
                                               o=o)
-            R.replayssm_gdn_spec_advance(d["kr"], slots, d["wp"], d["fl"], acc_t[i % 8], T,
-                                         inp_i["k"], d["nwp"], d["nfl"])
+            R.replayssm_gdn_spec_advance(d["kr"], d["gr"], d["vr"], d["br"], slots, d["wp"],
+                                         d["fl"], acc_t[i % 8], T, inp_i["k"], inp_i["v"],
+                                         inp_i["g"], inp_i["beta"], d["nwp"], d["nfl"])
             d["fl"], d["nfl"] = d["nfl"], d["fl"]
             f = d["f"]
             wv = np.where(f, 0, w)
             if count:
-                # a folding row: the tile write and its raw rows (the tile
-                # read is the verify's); the advance re-reads its drafts' k
-                per_row = (tile + wv * entry + T * (entry + V * sio + 4) + inp + 4) * HV \
-                    + np.where(f, (tile + w * raw) * HV + T * HK * K * sio, 0) + 18
+                # verify: the tile, committed d, k, g rows, the drafts' d rows,
+                # inputs and outputs; a folding row also writes its tile and
+                # reads its raw rows (the tile read is the verify's); advance:
+                # the kept drafts' v, k, g, beta rows read from the inputs
+                # and written to the ring, and the cursors
+                per_row = (tile + wv * entry + T * V * 4 + inp + 4) * HV \
+                    + np.where(f, (tile + w * raw) * HV, 0) + 2 * a * raw * HV + 18
                 bytes_total[0] += float(per_row.sum())
             d["w"] = wv + a
             d["f"] = d["w"] + T > L

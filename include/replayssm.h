@@ -384,24 +384,26 @@ int replayssm_gdn_spec_commit(const rssm_gdn_dims* dims, int32_t n_draft, void* 
  * [batch] uint8, required) first fold ring entries 0..write_pos[b]-1 into
  * the state exactly as replayssm_gdn_spec_commit does (0 <= write_pos[b] <=
  * L, else RSSM_ST_RING_OVERFLOW), store it, then verify their drafts at ring
- * entries 0..T-1; their drafts' k rows are left to
- * replayssm_gdn_spec_advance (the other value heads of the key head may
- * still be reading the old ones).  Other rows: as replayssm_gdn_spec_verify.
- * Arguments otherwise as replayssm_gdn_spec_verify, with the state written.
- * A folding row stages the k and v rows of the whole ring next to the
- * verify's own rows: RSSM_ESHAPE when they do not fit one workgroup's 64 KB
- * of LDS (at K = V = 128 the longest rings are 46 entries for T <= 4 and 42
- * for T = 8 with bf16 inputs, 27 and 24 with fp32 ones).
+ * entries 0..T-1 (w = 0); other rows verify at w = write_pos[b] as in
+ * replayssm_gdn_spec_verify (w + T <= L).  Writes o and the drafts' d rows
+ * at ring entries w..w+T-1 only: their v, k, g and beta rows are written by
+ * replayssm_gdn_spec_advance for the drafts kept.  Arguments otherwise as
+ * replayssm_gdn_spec_verify, with the state written.  A folding row stages
+ * the k and v rows of the whole ring next to the verify's own rows:
+ * RSSM_ESHAPE when they do not fit one workgroup's 64 KB of LDS (at K = V =
+ * 128 the longest rings are 46 entries for T <= 4 and 42 for T = 8 with bf16
+ * inputs, 27 and 24 with fp32 ones).
  *
  * replayssm_gdn_spec_advance - after the verify, with accepted[b] (0..T)
  * drafts kept: w = is_flush[b] ? 0 : write_pos[b]; w' = w + accepted[b];
  * next_write_pos[b] = w'; next_is_flush[b] = (w' + T > L) or
- * force_flush[b] (may be NULL).  Rows with is_flush[b] set also receive the
- * k rows of their T drafts (k [batch, T, HK, K] io_dtype [16B], this round's
- * verify input) at k_ring entries 0..T-1 of their key heads.  The next_*
- * buffers must not alias write_pos / is_flush.  dims as for the verify (only
- * batch, k_heads, dk, ring_len, num_slots and io_dtype are used).  accepted outside [0, T] sets RSSM_ST_RING_OVERFLOW and is clamped; a slot
- * out of range sets RSSM_ST_BAD_SLOT and its row is not marked.
+ * force_flush[b] (may be NULL).  The kept drafts' rows go from this round's
+ * verify inputs (k [batch, T, HK, K], v [batch, T, HV, V] io_dtype [16B];
+ * g, beta [batch, T, HV] float32) to ring entries w..w'-1 of k_ring (per key
+ * head), v_ring, g_ring and beta_ring.  The next_* buffers must not alias
+ * write_pos / is_flush.  dims as for the verify.  accepted outside [0, T]
+ * sets RSSM_ST_RING_OVERFLOW and is clamped; a slot out of range sets
+ * RSSM_ST_BAD_SLOT and its row is neither marked nor written.
  */
 int replayssm_gdn_spec_verify_flush(const rssm_gdn_dims* dims, int32_t n_draft,
                                     float* state, float* d_ring, void* k_ring,
@@ -413,7 +415,9 @@ int replayssm_gdn_spec_verify_flush(const rssm_gdn_dims* dims, int32_t n_draft,
                                     hipStream_t stream);
 
 int replayssm_gdn_spec_advance(const rssm_gdn_dims* dims, int32_t n_draft, void* k_ring,
-                               const void* k, const int32_t* slot_idx,
+                               float* g_ring, void* v_ring, float* beta_ring,
+                               const void* k, const void* v, const float* g,
+                               const float* beta, const int32_t* slot_idx,
                                const int32_t* write_pos, const uint8_t* is_flush,
                                const int32_t* accepted, const uint8_t* force_flush,
                                int32_t* next_write_pos, uint8_t* next_is_flush,

@@ -94,7 +94,7 @@ def load():
     lib.replayssm_gdn_spec_verify.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 16
     lib.replayssm_gdn_spec_commit.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 13
     lib.replayssm_gdn_spec_verify_flush.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 17
-    lib.replayssm_gdn_spec_advance.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 11
+    lib.replayssm_gdn_spec_advance.argtypes = [ctypes.POINTER(GdnDims), I] + [P] * 17
     lib.kda_standard_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 10
     lib.replayssm_kda_decode.argtypes = [ctypes.POINTER(GdnDims)] + [P] * 17
     for fn in ("ssu_standard_decode", "replayssm_decode", "replayssm_ring_reset",
@@ -538,20 +538,30 @@ def replayssm_gdn_spec_commit(state, k_ring, g_ring, v_ring, beta_ring, slot_idx
     _check("replayssm_gdn_spec_commit", rc)
 
 
-def replayssm_gdn_spec_advance(k_ring, slot_idx, write_pos, is_flush, accepted, n_draft, k,
-                               next_write_pos, next_is_flush, force_flush=None, status=None,
-                               stream=None):
+def replayssm_gdn_spec_advance(k_ring, g_ring, v_ring, beta_ring, slot_idx, write_pos, is_flush,
+                               accepted, n_draft, k, v, g, beta, next_write_pos, next_is_flush,
+                               force_flush=None, status=None, stream=None):
     """Cursor advance of the deferred-fold rounds (no fold here): a row that
-    folded in this round's verify (is_flush set) restarts from entry 0 and
-    receives its drafts' k rows (k [batch, T, HK, K], this round's input) at
-    ring entries 0..T-1; then w' = w + accepted and next_is_flush = (w' + T >
-    L) or force_flush."""
+    folded in this round's verify (is_flush set) restarts from entry 0; the
+    kept drafts' v, k, g, beta rows (this round's inputs: k [batch, T, HK,
+    K], v [batch, T, HV, V], g, beta [batch, T, HV]) go to their ring
+    entries; w' = w + accepted and next_is_flush = (w' + T > L) or
+    force_flush."""
     dev = k_ring.device
     io = k_ring.dtype
     _need(k_ring, "k_ring", (torch.float32, torch.bfloat16), dev=dev)
     ns, HK, L, K = k_ring.shape
+    _need(v_ring, "v_ring", io, dev=dev)
+    HV, V = v_ring.shape[1], v_ring.shape[3]
+    _need(v_ring, "v_ring", io, (ns, HV, L, V))
+    _need(g_ring, "g_ring", torch.float32, (ns, HV, L), dev=dev)
+    _need(beta_ring, "beta_ring", torch.float32, (ns, HV, L), dev=dev)
     nb = slot_idx.shape[0]
-    _need(k, "k", io, (nb, n_draft, HK, K), dev=dev)
+    T = n_draft
+    _need(k, "k", io, (nb, T, HK, K), dev=dev)
+    _need(v, "v", io, (nb, T, HV, V), dev=dev)
+    _need(g, "g", torch.float32, (nb, T, HV), dev=dev)
+    _need(beta, "beta", torch.float32, (nb, T, HV), dev=dev)
     _need(slot_idx, "slot_idx", torch.int32, (nb,), dev=dev)
     _need(write_pos, "write_pos", torch.int32, (nb,), dev=dev)
     _need(is_flush, "is_flush", torch.uint8, (nb,), dev=dev)
@@ -560,9 +570,10 @@ def replayssm_gdn_spec_advance(k_ring, slot_idx, write_pos, is_flush, accepted, 
     _need(next_is_flush, "next_is_flush", torch.uint8, (nb,), dev=dev)
     _opt(force_flush, "force_flush", torch.uint8, (nb,), dev=dev)
     _opt(status, "status", torch.int32, (1,))
-    d = GdnDims(nb, HK, HK, K, K, L, ns, F32, _DT[io], _DT[io], 0.0)  # value heads unused
+    d = GdnDims(nb, HK, HV, K, V, L, ns, F32, _DT[io], _DT[io], 0.0)
     rc = load().replayssm_gdn_spec_advance(
-        ctypes.byref(d), ctypes.c_int32(n_draft), _ptr(k_ring), _ptr(k), _ptr(slot_idx),
-        _ptr(write_pos), _ptr(is_flush), _ptr(accepted), _ptr(force_flush),
-        _ptr(next_write_pos), _ptr(next_is_flush), _ptr(status), _stream(stream))
+        ctypes.byref(d), ctypes.c_int32(T), _ptr(k_ring), _ptr(g_ring), _ptr(v_ring),
+        _ptr(beta_ring), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(slot_idx), _ptr(write_pos),
+        _ptr(is_flush), _ptr(accepted), _ptr(force_flush), _ptr(next_write_pos),
+        _ptr(next_is_flush), _ptr(status), _stream(stream))
     _check("replayssm_gdn_spec_advance", rc)

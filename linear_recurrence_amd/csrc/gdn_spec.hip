@@ -48,9 +48,11 @@
 // same recurrence on the verify's lane layout, row sums over 16 or 32 lanes
 // by row swaps and DPP), stores the folded tile and verifies the drafts at
 // entries 0..T-1, so the folding tile is read from memory once instead of
-// twice.  The drafts' k rows of such a row are written by the advance: in
-// the verify the other value heads of the key head may still be reading
-// the old ones for their own folds.
+// twice.  In these rounds the verify writes only the drafts' d rows; the
+// advance writes the kept drafts' v, k, g and beta rows from the inputs (in
+// the verify the other value heads of a folding row's key head may still
+// be reading its old k rows, and writes inside the tile read stream cost
+// several times their bytes).
 #include <math.h>
 
 #include "gdn_common.hpp"
@@ -605,12 +607,13 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
   // each array's T rows are one contiguous run in the ring, written by
   // consecutive lanes with non-temporal stores (written this way, scattered
   // ring writes inside the tile read stream cost a third of the per-row
-  // layout); then g and beta
-  // (after a fold the other value heads of this key head may still be
-  // reading its old k rows: those rows are written by the advance instead)
-  const bool k_writer = (hv % a.vpk) == 0 && !fold;
+  // layout); then g and beta.  The deferred-fold rounds (FL) write the d
+  // rows only: the advance writes the accepted drafts' v, k, g and beta
+  // rows from the inputs, outside this read stream (and after every value
+  // head of a folding row has read its old k rows).
+  const bool k_writer = !FL && (hv % a.vpk) == 0;
   {
-    const int nd = T * DV, nv = T * VV, nk = k_writer ? T * QV : 0;
+    const int nd = T * DV, nv = FL ? 0 : T * VV, nk = k_writer ? T * QV : 0;
     for (int e = tid; e < nd + nv + nk; e += NT) {
       if (e < nd) {
         const u32x4 x = *reinterpret_cast<const u32x4*>(lds + ((long)oD + w * DV + e) * 16);
@@ -626,6 +629,7 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
       }
     }
   }
+  if (FL) return;
   if (wave == 0) {
     if (lane >= w && lane < w + T) a.g_ring[gring0 + lane] = gl;
     if (lane < T) a.beta_ring[gring0 + w + lane] = bl;
@@ -959,47 +963,74 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_commit_ke
 // Cursor advance of the deferred-fold rounds, one workgroup per row: a row
 // that folded in this round's verify starts from entry 0, then keeps its
 // accepted drafts (commit_row); the next verify folds it when the flag is
-// set.  A row that folded also receives its drafts' k rows at ring entries
-// 0..T-1 here, not in the verify, where other value heads of its key head
-// may still have been reading the old rows.
-template <typename IT, int K>
+// set.  The kept drafts' v, k, g and beta rows go from this round's inputs
+// to their ring entries here (the verify wrote their d rows): written by a
+// launch of their own they do not interrupt the verify's tile reads, only
+// the kept drafts are written, and no value head of a folding row can
+// still be reading the old k rows of its key head.
+template <typename IT, int V, int K>
 __global__ void __launch_bounds__(256) gdn_spec_advance_kernel(const SpecArgs a) {
-  constexpr int QV = K / Elt<IT>::kPer16;
-  constexpr int NT = 256, B = 4;
+  constexpr int EPV = Elt<IT>::kPer16;
+  constexpr int QV = K / EPV, VV = V / EPV;
+  constexpr int NT = 256, B = 8;
   constexpr long kIo = sizeof(IT);
   const int r = blockIdx.x;
   const int tid = threadIdx.x;
-  const int T = a.n_draft, L = a.ring_len, HK = a.k_heads;
+  const int T = a.n_draft, L = a.ring_len, HK = a.k_heads, HV = a.v_heads;
   const int s = a.slot_idx[r];
   const bool folded = a.is_flush[r] != 0;
+  const int w = folded ? 0 : a.write_pos[r];
+  const CommitRow cr = commit_row(s, w, a.accepted[r], a.force_flush && a.force_flush[r], a);
   if (tid == 0) {
-    const CommitRow cr = commit_row(s, folded ? 0 : a.write_pos[r], a.accepted[r],
-                                    a.force_flush && a.force_flush[r], a);
     a.next_write_pos[r] = cr.wn;
     a.next_is_flush[r] = cr.flush ? 1 : 0;
     if (cr.st && a.status) atomicOr(a.status, cr.st);
   }
-  if (!folded || s < 0 || s >= a.num_slots) return;
-  // k rows of the T drafts: input [row, t, hk, K] -> ring [s, hk, t, K], in
-  // batches of B vectors per thread, every load of a batch before its stores
-  const int n = HK * T * QV;
-  const char* const ksrc = static_cast<const char*>(a.k) + (long)r * n * 16;
-  for (int u0 = 0; u0 < n; u0 += B * NT) {
+  const int w0 = w < 0 ? 0 : (w > L ? L : w);
+  // kept drafts (entries w0..wn-1, within the ring; at most the T inputs
+  // even when accepted is out of range)
+  const int na = cr.wn - w0 < T ? cr.wn - w0 : T;
+  if (na <= 0 || s < 0 || s >= a.num_slots) return;
+  // vectors: v rows [t][hv] then k rows [t][hk]; scalars: g and beta [t][hv];
+  // every load of a batch (clamped indices, no load in a branch) before its
+  // stores
+  const int nvv = na * HV * VV, nvec = nvv + na * HK * QV, nsc = na * HV;
+  for (int i = 0; i * B * NT < nvec || i * NT < nsc; ++i) {
+    const int u0 = i * B * NT, s0 = i * NT;  // this batch's vectors and scalars
     u32x4 x[B];
+    long dst[B];
+    bool isv[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
-      const int u = u0 + j * NT + tid;
-      x[j] = ld16(ksrc, (long)(u < n ? u : n - 1) * 16);  // clamped: no load in a branch
-    }
-#pragma unroll
-    for (int j = 0; j < B; ++j) {
-      const int u = u0 + j * NT + tid;
-      if (u < n) {
-        const int t = u / (HK * QV);
-        const int hk = (u - t * HK * QV) / QV;
-        const int c = u - (t * HK + hk) * QV;
-        st16(a.k_ring, ((((long)s * HK + hk) * L + t) * K) * kIo + (long)c * 16, x[j]);
+      const int uj = u0 + j * NT + tid;
+      const int u = uj < nvec ? uj : nvec - 1;
+      isv[j] = u < nvv;
+      if (u < nvv) {
+        const int t = u / (HV * VV);
+        const int hv = (u - t * HV * VV) / VV;
+        const int c = u - (t * HV + hv) * VV;
+        x[j] = ld16(a.v, (((long)(r * T + t) * HV + hv) * V) * kIo + (long)c * 16);
+        dst[j] = ((((long)s * HV + hv) * L + w0 + t) * V) * kIo + (long)c * 16;
+      } else {
+        const int uk = u - nvv;
+        const int t = uk / (HK * QV);
+        const int hk = (uk - t * HK * QV) / QV;
+        const int c = uk - (t * HK + hk) * QV;
+        x[j] = ld16(a.k, (((long)(r * T + t) * HK + hk) * K) * kIo + (long)c * 16);
+        dst[j] = ((((long)s * HK + hk) * L + w0 + t) * K) * kIo + (long)c * 16;
       }
+    }
+    const int us = s0 + tid < nsc ? s0 + tid : nsc - 1;
+    const int ts = us / HV, hs = us - ts * HV;
+    const long ssrc = (long)(r * T + ts) * HV + hs;
+    const float gv = a.g[ssrc], bv = a.beta[ssrc];
+#pragma unroll
+    for (int j = 0; j < B; ++j)
+      if (u0 + j * NT + tid < nvec) st16(isv[j] ? a.v_ring : a.k_ring, dst[j], x[j]);
+    if (s0 + tid < nsc) {
+      const long sdst = ((long)s * HV + hs) * L + w0 + ts;
+      a.g_ring[sdst] = gv;
+      a.beta_ring[sdst] = bv;
     }
   }
 }
@@ -1071,8 +1102,15 @@ static int commit_shape(const SpecArgs& a, const rssm_gdn_dims& d, hipStream_t s
 
 template <typename IT>
 static int launch_advance(const SpecArgs& a, const rssm_gdn_dims& d, hipStream_t s) {
-  const void* fn = d.dk == 128 ? reinterpret_cast<const void*>(&gdn_spec_advance_kernel<IT, 128>)
-                               : reinterpret_cast<const void*>(&gdn_spec_advance_kernel<IT, 64>);
+  const void* fn;
+  if (d.dv == 128 && d.dk == 128)
+    fn = reinterpret_cast<const void*>(&gdn_spec_advance_kernel<IT, 128, 128>);
+  else if (d.dv == 64 && d.dk == 64)
+    fn = reinterpret_cast<const void*>(&gdn_spec_advance_kernel<IT, 64, 64>);
+  else if (d.dv == 128 && d.dk == 64)
+    fn = reinterpret_cast<const void*>(&gdn_spec_advance_kernel<IT, 128, 64>);
+  else
+    fn = reinterpret_cast<const void*>(&gdn_spec_advance_kernel<IT, 64, 128>);
   return launch_kernel(fn, (unsigned)d.batch, 256, 0, s, a);
 }
 
@@ -1170,7 +1208,9 @@ extern "C" int replayssm_gdn_spec_verify_flush(
 }
 
 extern "C" int replayssm_gdn_spec_advance(const rssm_gdn_dims* dims, int32_t n_draft,
-                                          void* k_ring, const void* k,
+                                          void* k_ring, float* g_ring, void* v_ring,
+                                          float* beta_ring, const void* k, const void* v,
+                                          const float* g, const float* beta,
                                           const int32_t* slot_idx, const int32_t* write_pos,
                                           const uint8_t* is_flush, const int32_t* accepted,
                                           const uint8_t* force_flush, int32_t* next_write_pos,
@@ -1179,16 +1219,23 @@ extern "C" int replayssm_gdn_spec_advance(const rssm_gdn_dims* dims, int32_t n_d
   int rc = spec_check(dims, n_draft);
   if (rc) return rc;
   if (dims->batch == 0) return RSSM_OK;
-  if (!k_ring || !k || !slot_idx || !write_pos || !is_flush || !accepted || !next_write_pos ||
-      !next_is_flush)
+  if (!k_ring || !g_ring || !v_ring || !beta_ring || !k || !v || !g || !beta || !slot_idx ||
+      !write_pos || !is_flush || !accepted || !next_write_pos || !next_is_flush)
     return RSSM_EINVAL;
-  if (!aligned16(k_ring) || !aligned16(k)) return RSSM_EINVAL;
+  if (!aligned16(k_ring) || !aligned16(v_ring) || !aligned16(k) || !aligned16(v))
+    return RSSM_EINVAL;
   if ((const void*)next_write_pos == (const void*)write_pos ||
       (const void*)next_is_flush == (const void*)is_flush)
     return RSSM_EINVAL;
   SpecArgs a = spec_args(dims, n_draft);
   a.k_ring = k_ring;
+  a.g_ring = g_ring;
+  a.v_ring = v_ring;
+  a.beta_ring = beta_ring;
   a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
   a.slot_idx = slot_idx;
   a.write_pos = write_pos;
   a.is_flush = is_flush;

@@ -244,9 +244,9 @@ def run_spec_deferred(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torc
             assert (d <= bound).all(), f"round {r}: o error {d.max():.2e}"
         acc = rng.integers(0, T + 1, nb).astype(np.int32)
         force = (rng.random(nb) < force_p).astype(np.uint8)
-        R.replayssm_gdn_spec_advance(kr, sl, wp, fl, torch.tensor(acc, device=dev), T, k, nwp,
-                                     nfl, force_flush=torch.tensor(force, device=dev),
-                                     status=status)
+        R.replayssm_gdn_spec_advance(kr, gr, vr, br, sl, wp, fl, torch.tensor(acc, device=dev),
+                                     T, k, v, g, beta, nwp, nfl,
+                                     force_flush=torch.tensor(force, device=dev), status=status)
         o_wp, o_fl, ost = OS.gdn_spec_commit(o_pool, *o_rings[1:], o_sl, o_wp, acc[sample], T,
                                              force_flush=force[sample], state_dtype="f32")
         assert ost == 0
@@ -256,13 +256,22 @@ def run_spec_deferred(nb, HK, HV, K, V, L, T, io, rounds, sample, seed, out=torc
         np.testing.assert_array_equal(nfl.cpu().numpy(), nfl_ref)
         np.testing.assert_array_equal(o_fl, nfl_ref[sample])
         np.testing.assert_array_equal(o_wp, np.where(nfl_ref, 0, w_all)[sample])
-        # the drafts' k rows of rows that folded this round, written by the advance
-        krs = kr.cpu()
-        for row in np.flatnonzero(fl_now):
-            got_k = krs[int(slots[row]), :, :T, :]
-            want_k = k[row].cpu().permute(1, 0, 2)
-            assert torch.equal(got_k.view(torch.int16) if io == torch.bfloat16 else got_k,
-                               want_k.view(torch.int16) if io == torch.bfloat16 else want_k)
+        # the kept drafts' k, v, g and beta rows, written by the advance at
+        # entries w..w'-1 (bit copies of the inputs)
+        bits = (lambda t: t.view(torch.int16)) if io == torch.bfloat16 else (lambda t: t)
+        krs, vrs, grs, brs = kr.cpu(), vr.cpu(), gr.cpu(), br.cpu()
+        kc, vc, gc, bc = k.cpu(), v.cpu(), g.cpu(), beta.cpu()
+        w_eff = np.where(fl_now, 0, wp_now)
+        for row in range(nb):
+            s_, a_, w_ = int(slots[row]), int(acc[row]), int(w_eff[row])
+            if a_ == 0:
+                continue
+            assert torch.equal(bits(krs[s_, :, w_:w_ + a_, :]),
+                               bits(kc[row, :a_].permute(1, 0, 2).contiguous()))
+            assert torch.equal(bits(vrs[s_, :, w_:w_ + a_, :]),
+                               bits(vc[row, :a_].permute(1, 0, 2).contiguous()))
+            assert torch.equal(grs[s_, :, w_:w_ + a_], gc[row, :a_].t())
+            assert torch.equal(brs[s_, :, w_:w_ + a_], bc[row, :a_].t())
         wp, nwp = nwp, wp
         fl, nfl = nfl, fl
     torch.cuda.synchronize()

@@ -276,8 +276,9 @@ def test_gdn_spec_deferred_rounds_in_a_graph():
         R.replayssm_gdn_spec_verify_flush(d["state"], d["dr"], d["kr"], d["gr"], d["vr"],
                                           d["br"], slots, d["wp"], d["fl"], x["q"], x["k"],
                                           x["v"], x["g"], x["beta"], o=d["o"][k])
-        R.replayssm_gdn_spec_advance(d["kr"], slots, d["wp"], d["fl"], x["acc"], T, x["k"],
-                                     d["nwp"], d["nfl"], force_flush=x["force"])
+        R.replayssm_gdn_spec_advance(d["kr"], d["gr"], d["vr"], d["br"], slots, d["wp"], d["fl"],
+                                     x["acc"], T, x["k"], x["v"], x["g"], x["beta"], d["nwp"],
+                                     d["nfl"], force_flush=x["force"])
         d["wp"], d["nwp"] = d["nwp"], d["wp"]
         d["fl"], d["nfl"] = d["nfl"], d["fl"]
 

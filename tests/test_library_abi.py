@@ -99,14 +99,15 @@ def test_host_validation_rejects_bad_arguments_without_a_gpu():
                                                    None, None) == -4
     gd = R.GdnDims(2, 1, 2, 128, 128, 16, 4, 0, 1, 1, 0.0)
     A, B = V(0x2000), V(0x3000)
-    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, P, P, P, P, A, P, None, B, A,
+    rk = [P] * 8                              # k_ring .. beta
+    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, *rk, P, P, A, P, None, B, A,
                                           None, None) == -1        # next_is_flush aliases is_flush
-    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, P, P, P, B, A, P, None, B, P,
+    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, *rk, P, B, A, P, None, B, P,
                                           None, None) == -1        # next_write_pos aliases write_pos
-    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, P, P, P, P, A, None, None, B, P,
+    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, *rk, P, P, A, None, None, B, P,
                                           None, None) == -1        # no accepted
-    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, P, V(0x1008), P, P, A, P, None,
-                                          B, P, None, None) == -1  # misaligned k
+    assert lib.replayssm_gdn_spec_advance(ctypes.byref(gd), 4, P, P, P, P, P, V(0x1008), P, P,
+                                          P, P, A, P, None, B, P, None, None) == -1  # misaligned v
     # KDA: the gate rows are vector operands (16-byte alignment) and take LDS
     # of their own (at K = V = 128 a ring fits 48 entries with bf16 inputs)
     P = V(0x1000)
