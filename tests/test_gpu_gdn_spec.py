@@ -328,6 +328,12 @@ def test_spec_deferred_full_size_bf16_output():
                       seed=14, out=torch.bfloat16, drain=True)
 
 
+def test_spec_deferred_many_heads():
+    """64 value heads and 8 drafts: the advance copies its kept drafts' rows
+    in several batches of vectors and of gates per row."""
+    run_spec_deferred(8, 16, 64, 128, 128, 16, 8, torch.bfloat16, 8, range(8), seed=94)
+
+
 def test_spec_deferred_large_batch():
     """520 rows (one advance workgroup per row; the verify's grid in batch
     order), fp32 inputs, drained at the end."""
