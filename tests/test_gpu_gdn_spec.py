@@ -1,7 +1,9 @@
 """GDN speculative verify and commit on the GPU against the float64 oracle:
 rounds of verify -> random acceptance -> commit (with exact folds whenever the
 next verify would not fit, and forced folds), checking every draft output,
-every cursor and every folded state."""
+every cursor and every folded state; and the deferred-fold rounds (verify
+with flush -> random acceptance -> advance) against the oracle's rounds on
+the same inputs."""
 
 import numpy as np
 import pytest
