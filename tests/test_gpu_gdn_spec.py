@@ -382,7 +382,9 @@ def test_spec_deferred_too_long_ring_is_refused():
 def test_spec_deferred_bad_cursor_is_refused():
     """A folding row past the ring (w > L) and an other row whose drafts do
     not fit (w + T > L) are refused with the status bit and NaN outputs;
-    the good rows are verified."""
+    the good rows are verified.  The advance with accepted counts out of
+    range sets the status bit, clamps the cursor to the ring and copies at
+    most the T drafts."""
     print("case: deferred spec bad cursors", flush=True)
     dev = torch.device("cuda:0")
     HK, HV, K, V, L, T = 1, 2, 64, 64, 8, 4
@@ -402,6 +404,22 @@ def test_spec_deferred_bad_cursor_is_refused():
     assert status.item() & R.ST_RING_OVERFLOW
     assert torch.isnan(o[1]).all() and torch.isnan(o[2]).all()
     assert torch.isfinite(o[0]).all() and torch.isfinite(o[3]).all()
+    # accepted counts out of range: the status bit, the cursor clamped to the
+    # ring, at most T kept drafts copied
+    status.zero_()
+    wp2 = torch.tensor([0, 6, 2, 0], dtype=torch.int32, device=dev)
+    fl2 = torch.zeros(4, dtype=torch.uint8, device=dev)
+    acc = torch.tensor([T + 1, 4, -1, 2], dtype=torch.int32, device=dev)
+    nwp = torch.empty(4, dtype=torch.int32, device=dev)
+    nfl = torch.empty(4, dtype=torch.uint8, device=dev)
+    kr, gr, vr, br = rings[1], rings[2], rings[3], rings[4]
+    R.replayssm_gdn_spec_advance(kr, gr, vr, br, sl, wp2, fl2, acc, T, q, v, gb, gb, nwp, nfl,
+                                 status=status)
+    torch.cuda.synchronize()
+    assert status.item() & R.ST_RING_OVERFLOW
+    assert nwp.cpu().tolist() == [T + 1, 8, 1, 2]
+    assert nfl.cpu().tolist() == [1, 1, 0, 0]
+    assert torch.equal(kr[0, 0, :T], q[0, :, 0]) and (kr[0, 0, T:] == 0).all()
 
 
 def test_spec_bad_cursor_is_refused():
