@@ -168,7 +168,7 @@ __global__ void __launch_bounds__((GdnShape<V, K, REPLAY>::NT)) gdn_decode_kerne
       const int u = j + lane;
       if (u < n) {
         const char* src = u < nring ? ring + (long)u * 16 : cur + (long)(u - nring) * 16;
-        dma16(src, lds + (long)(c0 + j) * 16);
+        dma16<REPLAY>(src, lds + (long)(c0 + j) * 16);
       }
     }
   };

@@ -570,7 +570,7 @@ __global__ void __launch_bounds__((TileShape<ST, P, N, PER>::NT), (kMinWaves<ST,
       const int u = j + lane;
       if (u < n) {
         const char* src = u < nring ? ring + (long)u * 16 : cur + (long)(u - nring) * 16;
-        dma16(src, lds + (long)(c0 + j) * 16);
+        dma16<REPLAY>(src, lds + (long)(c0 + j) * 16);
       }
     }
   };

@@ -284,9 +284,13 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // 16 bytes per lane from global memory straight into LDS (no VGPRs): lane l
 // of the issuing wave writes lds_wave_base + 16*l.  The base must be uniform
-// across the wave.
+// across the wave.  NT: the non-temporal policy (aux 2), for rows read once
+// per step beside the state tile (the ring decode kernels' staging: measured
+// faster there; rows that other workgroups of the launch read too stay
+// temporal).
+template <bool NT = false>
 __device__ static inline void dma16(const void* gsrc, void* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_wave_base, 16, 0, 0);
+  __builtin_amdgcn_global_load_lds(gsrc, (lds_void*)lds_wave_base, 16, 0, NT ? 2 : 0);
 }
 
 // Raw element reads from LDS, converted to fp32.
