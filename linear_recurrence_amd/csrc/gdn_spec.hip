@@ -161,12 +161,16 @@ constexpr size_t verify_fold_bytes(int L) {
 }
 
 // 16-byte chunks [c0, c0+n) of LDS from global memory, one wave-wide
-// direct-to-LDS load per 64 chunks; chunk u comes from src + 16*u.
+// direct-to-LDS load per 64 chunks; chunk u comes from src + 16*u.  NT: the
+// non-temporal policy, for rows only this workgroup reads (a value head's
+// own v and d rows; the q and k rows are shared by the value heads of a key
+// head and stay temporal).
+template <bool NT = false>
 __device__ static inline void dma_rows(char* lds, int c0, int n, const char* src, int wave,
                                        int lane, int nt) {
   for (int j = wave * 64; j < n; j += nt) {
     const int u = j + lane;
-    if (u < n) dma16(src + (long)u * 16, lds + (long)(c0 + j) * 16);
+    if (u < n) dma16<NT>(src + (long)u * 16, lds + (long)(c0 + j) * 16);
   }
 }
 
@@ -355,19 +359,19 @@ __global__ void __launch_bounds__((GdnShape<V, K, true>::NT)) gdn_spec_verify_ke
     const long qk = ((long)(b * T + t) * HK + hk) * K;
     dma_rows(lds, t * QV, QV, (const char*)a.q + qk * kIo, wave, lane, NT);
     dma_rows(lds, oK + (w + t) * QV, QV, (const char*)a.k + qk * kIo, wave, lane, NT);
-    dma_rows(lds, oV + t * VV, VV, (const char*)a.v + ((long)(b * T + t) * HV + hv) * V * kIo,
-             wave, lane, NT);
+    dma_rows<true>(lds, oV + t * VV, VV,
+                   (const char*)a.v + ((long)(b * T + t) * HV + hv) * V * kIo, wave, lane, NT);
   }
   if (w > 0) {
     dma_rows(lds, oK, w * QV, (const char*)a.k_ring + kring0 * kIo, wave, lane, NT);
-    dma_rows(lds, oD, w * DV, (const char*)(a.d_ring + dring0), wave, lane, NT);
+    dma_rows<true>(lds, oD, w * DV, (const char*)(a.d_ring + dring0), wave, lane, NT);
   }
   // a folding row's raw k and v rows, after the verify's own regions
   char* const Fs = lds + verify_lds_bytes<IT, V, K, MF>(T, L);
   if constexpr (FL) {
     if (wf > 0) {
       dma_rows(Fs, 0, wf * QV, (const char*)a.k_ring + kring0 * kIo, wave, lane, NT);
-      dma_rows(Fs, L * QV, wf * VV, (const char*)a.v_ring + dring0 * kIo, wave, lane, NT);
+      dma_rows<true>(Fs, L * QV, wf * VV, (const char*)a.v_ring + dring0 * kIo, wave, lane, NT);
     }
   }
   // gates: committed (or folded) entries from the ring, the drafts from the
