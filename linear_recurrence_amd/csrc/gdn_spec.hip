@@ -42,13 +42,13 @@
 // then the rank-1 update (the waves never wait for one another); the tile is
 // stored scaled by the product.
 //
-// Deferred-fold rounds: the commit only advances the cursors and marks the
-// rows whose next verify would not fit (a per-row is_flush flag); that
-// verify folds their ring on the tile registers it has just loaded (the
-// same recurrence on the verify's lane layout, row sums over 16 or 32 lanes
-// by row swaps and DPP), stores the folded tile and verifies the drafts at
-// entries 0..T-1, so the folding tile is read from memory once instead of
-// twice.  In these rounds the verify writes only the drafts' d rows; the
+// Deferred-fold rounds: instead of the commit, an advance only moves the
+// cursors and marks the rows whose next verify would not fit (a per-row
+// is_flush flag); that verify folds their ring on the tile registers it has
+// just loaded (the same recurrence on the verify's lane layout, row sums
+// over 16 or 32 lanes by row swaps and DPP), stores the folded tile and
+// verifies the drafts at entries 0..T-1, so the folding tile is read from
+// memory once instead of twice.  In these rounds the verify writes only the drafts' d rows; the
 // advance writes the kept drafts' v, k, g and beta rows from the inputs (in
 // the verify the other value heads of a folding row's key head may still
 // be reading its old k rows, and writes inside the tile read stream cost
