@@ -98,3 +98,49 @@ def test_forced_flush_and_bad_cursors():
                                tok["q"][d][None], tok["k"][d][None], tok["v"][d][None],
                                tok["g"][d][None], tok["beta"][d][None])
     assert st & ST_RING_OVERFLOW and np.isnan(o).all()
+
+
+@pytest.mark.parametrize("L,T", [(8, 3), (16, 4), (2, 1)])
+def test_deferred_fold_rounds_match_the_recurrence(L, T):
+    """The deferred-fold rounds composed from the same oracle steps: the
+    advance keeps w' = (folded ? 0 : w) + accepted and marks the row when
+    w' + T > L (or forced); the next verify first folds entries 0..w'-1 by
+    the exact recurrence and verifies at entry 0.  Every draft output equals
+    the recurrence over the committed history plus the drafts before it, and
+    every fold equals the recurrent state: the rule keeps each verify inside
+    the ring and loses no committed token."""
+    rng = np.random.default_rng(L * 100 + T)
+    HK, HV, K, V = 2, 4, 3, 5
+    S_init = rng.normal(0, 0.2, (HV, V, K))
+    n_tok = 160
+    tok = _tokens(rng, n_tok, HK, HV, K, V)
+    state = S_init[None].copy()
+    rings = [np.full((1, HV, L, V), np.nan), np.full((1, HK, L, K), np.nan),
+             np.full((1, HV, L), np.nan), np.full((1, HV, L, V), np.nan),
+             np.full((1, HV, L), np.nan)]
+    kh = np.arange(HV) // (HV // HK)
+    w, flag = 0, False
+    committed, nxt, folds = [], 0, 0
+    while nxt + T <= n_tok:
+        if flag:
+            state[0] = OS.exact_fold(state[0], rings[1], rings[2], rings[3], rings[4], 0, w, kh)
+            _, S_ref = _recurrent_outputs(S_init, tok, committed)
+            np.testing.assert_allclose(state[0], S_ref, rtol=1e-9, atol=1e-12)
+            folds += 1
+            w = 0
+        assert w + T <= L
+        drafts = list(range(nxt, nxt + T))
+        nxt += T
+        o, st = OS.gdn_spec_verify(state, *rings, np.array([0]), np.array([w], np.int32),
+                                   tok["q"][drafts][None], tok["k"][drafts][None],
+                                   tok["v"][drafts][None], tok["g"][drafts][None],
+                                   tok["beta"][drafts][None])
+        assert st == 0
+        ref, _ = _recurrent_outputs(S_init, tok, committed + drafts)
+        for t in range(T):
+            np.testing.assert_allclose(o[0, t], ref[len(committed) + t], rtol=1e-9, atol=1e-12)
+        a = int(rng.integers(0, T + 1))
+        committed += drafts[:a]
+        w += a
+        flag = w + T > L or rng.random() < 0.1
+    assert folds > 0
